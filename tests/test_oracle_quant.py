@@ -1,0 +1,194 @@
+"""Pins for the oracle's group quantizers.
+
+Method (DeepSeek-V3 report, Section 3.3.2, Figure 7(a)): activations are
+scaled per 1x128 tile (per token, per 128 channels), weights per 128x128
+block; each group's maximum absolute value is taken online and mapped onto the
+largest E4M3 value.  Readings: dequantization scale s = fl32(amax/448),
+quantization multiplies by inv = min(fl32(448/amax), FLT_MAX).
+"""
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_quant_amd import synth
+
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+
+def _dec(codes):
+    """E4M3 values of non-NaN codes, from the bit layout s eeee mmm."""
+    vals = np.empty(codes.shape, dtype=np.float32)
+    for b in range(256):
+        if (b & 0x7F) == 0x7F:
+            continue
+        e, m = (b >> 3) & 15, b & 7
+        mag = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        vals[codes == b] = -mag if b & 0x80 else mag
+    return vals
+
+
+def _exact_groups(rng, rows, cols, s0, bf16=False):
+    """Inputs that are E4M3 values times a power of two, each 1x128 group
+    holding one +-448 code: the quantizer must return s == s0 and the very
+    codes the input was built from."""
+    codes = rng.integers(0, 256, size=(rows, cols)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3A            # no NaN codes
+    codes[(codes & 0x7F) == 0x7E] = 0x3B            # exactly one 448 per group:
+    for g in range(0, cols, 128):
+        w = min(128, cols - g)
+        pos = rng.integers(0, w, size=rows)
+        sign = rng.integers(0, 2, size=rows).astype(np.uint8) << 7
+        codes[np.arange(rows), g + pos] = 0x7E | sign
+    vals = _dec(codes)
+    x = (vals * np.float32(s0)).astype(np.float32)
+    assert np.array_equal(x / np.float32(s0), vals)   # exact scaling
+    if bf16:
+        xb = synth.f32_to_bf16_bits(x)
+        assert np.array_equal(synth.bf16_bits_to_f32(xb), x)   # <= 4 significant bits
+        return xb, codes
+    return x, codes
+
+
+@pytest.mark.parametrize("s0_exp", [-12, -3, 0, 7])
+@pytest.mark.parametrize("bf16", [False, True])
+def test_quant_1x128_exactly_representable(oracle, s0_exp, bf16):
+    rng = np.random.default_rng(100 + s0_exp)
+    s0 = np.float32(2.0 ** s0_exp)
+    x, codes = _exact_groups(rng, 37, 384, s0, bf16)
+    q, s = oracle.quant_1x128(x)
+    assert np.array_equal(q, codes)
+    assert np.all(s == s0) and s.shape == (3, 37)
+
+
+def test_quant_128x128_exactly_representable(oracle):
+    rng = np.random.default_rng(5)
+    s0 = np.float32(2.0 ** -5)
+    # one 448 per 128x128 block: build per-row groups, then keep only one
+    # 448 per block by demoting the others
+    x, codes = _exact_groups(rng, 256, 256, s0)
+    for bi in range(2):
+        for bj in range(2):
+            blk = codes[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            r, c = np.nonzero((blk & 0x7F) == 0x7E)
+            for rr, cc in zip(r[1:], c[1:]):
+                blk[rr, cc] = 0x3B | (blk[rr, cc] & 0x80)
+    x = (_dec(codes) * s0).astype(np.float32)
+    q, s, qt = oracle.quant_128x128(x, with_transpose=True)
+    assert np.array_equal(q, codes)
+    assert np.all(s == s0) and s.shape == (2, 2)
+    assert np.array_equal(qt, q.T)
+
+
+def test_group_scale_rule(oracle):
+    s, inv = oracle.group_scale(448.0)
+    assert s == 1.0 and inv == 1.0
+    s, inv = oracle.group_scale(0.0)
+    assert s == 0.0 and not np.signbit(s) and inv == FLT_MAX
+    s, inv = oracle.group_scale(1e-37)          # 448/amax overflows FP32
+    assert inv == FLT_MAX and s > 0
+    s, inv = oracle.group_scale(3.0e-43)        # amax/448 underflows to zero
+    assert s == 0.0
+    s, inv = oracle.group_scale(np.float32(3.2e-43))
+    assert s > 0.0                               # smallest subnormal survives
+    # a value whose quotient needs correct rounding: compare with exact
+    # rational arithmetic rounded to FP32 by numpy's IEEE division
+    for a in np.random.default_rng(0).uniform(1e-3, 1e3, 1000).astype(np.float32):
+        s, inv = oracle.group_scale(a)
+        assert s == np.float32(a) / np.float32(448)
+        assert inv == np.float32(448) / np.float32(a)
+
+
+def test_quant_all_zero_and_signs(oracle):
+    x = np.zeros((3, 256), dtype=np.float32)
+    x[1, :128] = -0.0
+    x[2, 5] = -1e-3
+    q, s = oracle.quant_1x128(x)
+    assert np.all(s.view(np.uint32)[:, :2] == 0)           # +0.0 scales
+    assert np.all(q[0] == 0x00)
+    assert np.all(q[1, :128] == 0x80) and np.all(q[1, 128:] == 0x00)
+    assert q[2, 5] == 0xFE and s[0, 2] == np.float32(1e-3) / np.float32(448)
+
+
+def test_quant_amax_element_saturates_to_448(oracle):
+    a, _ = synth.tiny_inputs()
+    q, s = oracle.quant_1x128(a)
+    for r in range(a.shape[0]):
+        for g in range(4):
+            grp = a[r, g * 128:(g + 1) * 128]
+            i = np.argmax(np.abs(grp))
+            assert (q[r, g * 128 + i] & 0x7F) == 0x7E
+
+
+def test_quant_error_bound(oracle):
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((64, 1024)) * np.exp(rng.uniform(-8, 8, (64, 1)))).astype(np.float32)
+    q, s = oracle.quant_1x128(x)
+    deq = oracle.e4m3_decode(q) * np.repeat(s.T.astype(np.float64), 128, axis=1)
+    err = np.abs(deq - x.astype(np.float64))
+    sc = np.repeat(s.T.astype(np.float64), 128, axis=1)
+    # E4M3 normals carry 3 mantissa bits (half-ulp 2^-4 relative); subnormal
+    # spacing is 2^-9, so half a step is 2^-10 in units of the scale; inv*s
+    # differs from 1 by a few FP32 ulps.
+    bound = (2.0 ** -4 * np.abs(x) + 2.0 ** -10 * sc) * (1 + 2.0 ** -20)
+    assert np.all(err <= bound)
+
+
+def test_quant_1x128_ragged_and_transposed_view(oracle):
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((200, 300)).astype(np.float32)
+    q, s = oracle.quant_1x128(x)
+    assert s.shape == (3, 200)
+    # last group has 44 columns: its scale follows only those columns
+    assert np.all(s[2] == np.abs(x[:, 256:]).max(axis=1) / np.float32(448))
+    # 128x1 groups on x == 1x128 groups on x^T
+    qt, st = oracle.quant_1x128(x, transposed=True)
+    q2, s2 = oracle.quant_1x128(np.ascontiguousarray(x.T))
+    assert np.array_equal(qt, q2) and np.array_equal(st, s2)
+    # bf16 input of the same values gives the same result
+    xb = synth.f32_to_bf16_bits(x)
+    q3, s3 = oracle.quant_1x128(xb)
+    q4, s4 = oracle.quant_1x128(synth.bf16_bits_to_f32(xb))
+    assert np.array_equal(q3, q4) and np.array_equal(s3, s4)
+
+
+def test_quant_gather_commutes(oracle):
+    rng = np.random.default_rng(12)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((300, 512)).astype(np.float32))
+    perm = rng.permutation(300)[:250]
+    q, s = oracle.quant_1x128(x)
+    qg, sg = oracle.quant_1x128(x[perm])
+    assert np.array_equal(qg, q[perm]) and np.array_equal(sg, s[:, perm])
+
+
+def test_quant_128x128_ragged_blocks(oracle):
+    rng = np.random.default_rng(13)
+    w = rng.standard_normal((300, 200)).astype(np.float32)
+    q, s, qt = oracle.quant_128x128(w, with_transpose=True)
+    assert s.shape == (3, 2)
+    for bi in range(3):
+        for bj in range(2):
+            blk = w[bi * 128:(bi + 1) * 128, bj * 128:(bj + 1) * 128]
+            assert s[bi, bj] == np.abs(blk).max() / np.float32(448)
+    assert np.array_equal(qt, q.T)
+
+
+def test_quant_matches_torch_library_cast(oracle):
+    """Grouping and scale rule written with torch tensor ops, encoding done by
+    torch's own float8_e4m3fn cast: after scaling, |x*inv| <= 448*(1+2^-23),
+    a range where the library cast and the saturating encoder agree."""
+    a, w = synth.tiny_inputs()
+    q, s = oracle.quant_1x128(a)
+    t = torch.from_numpy(a).view(256, 4, 128)
+    amax = t.abs().amax(dim=2)
+    inv = torch.clamp(torch.tensor(448.0) / amax, max=float(FLT_MAX))
+    ref_q = (t * inv[..., None]).to(torch.float8_e4m3fn).view(torch.uint8).reshape(256, 512)
+    assert np.array_equal(q, ref_q.numpy())
+    assert np.array_equal(s, (amax / 448.0).T.contiguous().numpy())
+    qw, sw, _ = oracle.quant_128x128(w)
+    tw = torch.from_numpy(w).view(2, 128, 4, 128).permute(0, 2, 1, 3)
+    amax = tw.abs().amax(dim=(2, 3))
+    inv = torch.clamp(torch.tensor(448.0) / amax, max=float(FLT_MAX))
+    ref = (tw * inv[..., None, None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    ref = ref.permute(0, 2, 1, 3).reshape(256, 512)
+    assert np.array_equal(qw, ref.numpy())
+    assert np.array_equal(sw, (amax / 448.0).numpy())
