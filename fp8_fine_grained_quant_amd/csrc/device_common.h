@@ -1,0 +1,57 @@
+// device_common.h -- small gfx950 device helpers shared by the quantize and
+// GEMM kernels of libfp8q.  Internal header; not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+// Largest finite OCP E4M3 magnitude: 1.75 * 2^8.
+constexpr float kE4M3Max = 448.0f;
+constexpr float kFltMax = 3.402823466e+38f;
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even FP32 -> BF16 bit pattern (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Max over the 16 lanes of a DPP row, on non-negative FP32 values compared
+// as unsigned integers (their bit patterns order like the values).
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // row_ror:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // row_ror:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // row_ror:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // row_ror:1
+    return v;
+}
+
+// Group scale rule: s = amax/448 (dequantization factor) and
+// inv = min(448/amax, FLT_MAX), both correctly rounded FP32 divisions
+// (amax == 0 gives 448/0 = +inf, clamped to FLT_MAX).
+__device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
+    s = amax / kE4M3Max;
+    inv = fminf(kE4M3Max / amax, kFltMax);
+}
+
+// Encode 4 FP32 values (already multiplied by inv) into one dword, byte i =
+// code of v_i.  Each value is clamped to +-448 first (saturation), then
+// converted by the hardware's round-to-nearest-even FP32 -> OCP E4M3
+// conversion, two values per instruction into one 16-bit half.
+__device__ __forceinline__ uint32_t enc4(float v0, float v1, float v2, float v3) {
+    v0 = __builtin_amdgcn_fmed3f(v0, -kE4M3Max, kE4M3Max);
+    v1 = __builtin_amdgcn_fmed3f(v1, -kE4M3Max, kE4M3Max);
+    v2 = __builtin_amdgcn_fmed3f(v2, -kE4M3Max, kE4M3Max);
+    v3 = __builtin_amdgcn_fmed3f(v3, -kE4M3Max, kE4M3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);
+    return (uint32_t)w;
+}
+
+}  // namespace fp8q

@@ -1,0 +1,50 @@
+// kernels.h -- internal launchers of libfp8q (host side).  Arguments are
+// assumed validated by fp8q_api.hip; every launcher returns the HIP error of
+// the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8q {
+
+enum { kF32 = 0, kBF16 = 1 };
+enum { kTileBlock = 0, kTileCols = 1 };
+enum { kScaleBlock128 = 0, kScaleRow128 = 1 };
+
+// 1x128 groups along contiguous rows of x[rows, cols] (row pitch ldx elements).
+hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream);
+
+// 128x128 tiles of x[rows, cols] (row pitch ldx).  kTileBlock: one scale per
+// tile, s[ti*ceil(cols/128)+tj], codes to q (row-major) and/or qt
+// (transposed).  kTileCols: one scale per column per 128 rows,
+// s[ti*lds + col], codes to qt only.
+hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
+                              int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
+                              float* s, int64_t lds, hipStream_t stream);
+
+struct GemmParams {
+    const uint8_t* a;
+    int64_t lda;
+    const float* sa;
+    int64_t ldsa;
+    const uint8_t* b;
+    int64_t ldb;
+    const float* sb;
+    int64_t sbs0, sbs1;
+    void* c;
+    int64_t ldc;
+    int64_t M, N, K;
+    // grouped GEMM only
+    const int32_t* offsets;
+    int64_t num_groups;
+};
+
+hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, hipStream_t stream);
+hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, hipStream_t stream);
+
+// Largest group count the grouped GEMM's on-chip tile table holds.
+constexpr int64_t kMaxGroups = 4096;
+
+}  // namespace fp8q

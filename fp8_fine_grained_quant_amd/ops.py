@@ -1,0 +1,223 @@
+"""Python binding of libfp8q (include/fp8q.h), same names as the C entry points.
+
+Only argument marshalling happens here: tensor shapes and strides become the
+C sizes and leading dimensions, outputs are allocated with torch when not
+given, and the call is enqueued on the current HIP stream of the tensors'
+device.  All arithmetic runs in the library's HIP kernels.  If the library
+has not been built, importing this module raises ImportError -- there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfp8q.so")
+
+F32, BF16 = 0, 1
+SCALE_BLOCK128, SCALE_ROW128 = 0, 1
+_STATUS = {0: "FP8Q_OK", 1: "FP8Q_EINVAL", 2: "FP8Q_EALIGN", 3: "FP8Q_EUNSUPPORTED",
+           4: "FP8Q_EHIP"}
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load_library():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build the HIP library first "
+            "(python -m fp8_fine_grained_quant_amd.build, or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.fp8_quant_1x128.restype = I
+    lib.fp8_quant_1x128.argtypes = [P, I, I64, I64, I64, I64, P, I64, P, I64, P]
+    lib.fp8_quant_128x128.restype = I
+    lib.fp8_quant_128x128.argtypes = [P, I, I64, I64, I64, P, I64, P, P, I64, P]
+    lib.fp8_blockscaled_gemm.restype = I
+    lib.fp8_blockscaled_gemm.argtypes = [P, I64, P, I64, P, I64, P, I, I64, I64, P, I, I64, I64,
+                                         I64, I64, P]
+    lib.fp8_grouped_gemm.restype = I
+    lib.fp8_grouped_gemm.argtypes = [P, I64, P, I64, P, I64, P, P, I64, I64, P, I, I64, I64,
+                                     I64, P]
+    lib.fp8q_status_string.restype = ctypes.c_char_p
+    lib.fp8q_status_string.argtypes = [I]
+    return lib
+
+
+_lib = _load_library()
+
+
+class Fp8qError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {fp8q_status_string(status)}")
+
+
+def fp8q_status_string(status: int) -> str:
+    return _lib.fp8q_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Fp8qError(status, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: torch.Tensor | None):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libfp8q operates on device tensors")
+
+
+# --- quantization -------------------------------------------------------------
+
+def fp8_quant_1x128(x: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,
+                    s: torch.Tensor | None = None):
+    """1x128 tile quantization of a 2-D activation tensor (bf16 or fp32).
+
+    transposed=False: groups of 128 along dim 1; returns q [R, C] uint8 codes
+    and s [ceil(C/128), R] FP32 scales.
+    transposed=True: groups of 128 along dim 0 (128x1 on the stored tensor,
+    for the weight-gradient GEMM); returns the codes of x^T, q [C, R], and
+    s [ceil(R/128), C].
+    """
+    _require_cuda(x)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    R, C = x.shape
+    if not transposed:
+        if x.stride(1) != 1:
+            raise ValueError("x must be contiguous along dim 1")
+        rows, cols, xs_r, xs_c = R, C, x.stride(0), 1
+    else:
+        if x.stride(1) != 1:
+            raise ValueError("x must be contiguous along dim 1")
+        rows, cols, xs_r, xs_c = C, R, 1, x.stride(0)
+    g = (cols + 127) // 128
+    if q is None:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    if s is None:
+        s = torch.empty((g, rows), dtype=torch.float32, device=x.device)
+    _require_cuda(q, s)
+    st = _lib.fp8_quant_1x128(_ptr(x), _dtype_code(x), rows, cols, xs_r, xs_c, _ptr(q),
+                              q.stride(0), _ptr(s), s.stride(0), _stream(x))
+    _check(st, "fp8_quant_1x128")
+    return q, s
+
+
+def fp8_quant_128x128(w: torch.Tensor, with_transpose: bool = False,
+                      q: torch.Tensor | None = None, s: torch.Tensor | None = None,
+                      q_t: torch.Tensor | None = None):
+    """128x128 block quantization of a 2-D weight (bf16 or fp32).
+
+    Returns q [R, C] codes, s [ceil(R/128), ceil(C/128)] scales and, if
+    requested, the transposed codes q_t [C, R]."""
+    _require_cuda(w)
+    if w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be 2-D and contiguous along dim 1")
+    R, C = w.shape
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=w.device)
+    if s is None:
+        s = torch.empty(((R + 127) // 128, (C + 127) // 128), dtype=torch.float32,
+                        device=w.device)
+    if with_transpose and q_t is None:
+        q_t = torch.empty((C, R), dtype=torch.uint8, device=w.device)
+    _require_cuda(q, s, q_t)
+    if not s.is_contiguous():
+        raise ValueError("s must be contiguous")
+    st = _lib.fp8_quant_128x128(_ptr(w), _dtype_code(w), R, C, w.stride(0), _ptr(q), q.stride(0),
+                                _ptr(s), _ptr(q_t), q_t.stride(0) if q_t is not None else 0,
+                                _stream(w))
+    _check(st, "fp8_quant_128x128")
+    return q, s, q_t
+
+
+# --- GEMM -------------------------------------------------------------------
+
+def _out_code(dtype) -> int:
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError("output dtype must be bfloat16 or float32")
+
+
+def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
+                         out_dtype=torch.bfloat16, scale_mode: int = SCALE_BLOCK128,
+                         c: torch.Tensor | None = None):
+    """C = A * B^T with per-128-K promotion.
+
+    a [M, K] and b [N, K] uint8 E4M3 codes (K contiguous); sa [K/128, M]
+    (any row pitch); sb: SCALE_BLOCK128 -> 2-D [ceil(N/128), K/128] (any
+    strides, e.g. a transposed view); SCALE_ROW128 -> [K/128, N] (row pitch
+    >= N)."""
+    _require_cuda(a, sa, b, sb)
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K or a.stride(1) != 1 or b.stride(1) != 1:
+        raise ValueError("a, b must be [M,K] / [N,K] with K contiguous")
+    if sa.stride(1) != 1:
+        raise ValueError("sa must be contiguous along dim 1")
+    if scale_mode == SCALE_BLOCK128:
+        sbs0, sbs1 = sb.stride(0), sb.stride(1)
+    else:
+        if sb.stride(1) != 1:
+            raise ValueError("ROW128 sb must be contiguous along dim 1")
+        sbs0, sbs1 = sb.stride(0), 0
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    _require_cuda(c)
+    if c.stride(1) != 1:
+        raise ValueError("c must be contiguous along dim 1")
+    st = _lib.fp8_blockscaled_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b),
+                                   b.stride(0), _ptr(sb), scale_mode, sbs0, sbs1, _ptr(c),
+                                   _out_code(c.dtype), c.stride(0), M, N, K, _stream(a))
+    _check(st, "fp8_blockscaled_gemm")
+    return c
+
+
+def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: torch.Tensor,
+                     offsets: torch.Tensor, out_dtype=torch.bfloat16,
+                     c: torch.Tensor | None = None):
+    """Per-group GEMM: rows [offsets[g], offsets[g+1]) of A times W_g^T.
+
+    a [M_total, K] codes, sa [K/128, M_total]; w [G, N, K] codes (contiguous
+    per group), sw [G, ceil(N/128), K/128] contiguous; offsets int32 [G+1] on
+    the device."""
+    _require_cuda(a, sa, w, sw, offsets)
+    M, K = a.shape
+    G, N, K2 = w.shape
+    if K2 != K or a.stride(1) != 1 or w.stride(2) != 1 or w.stride(0) != N * w.stride(1):
+        raise ValueError("a [M,K], w [G,N,K] with K contiguous and groups dense")
+    if not sw.is_contiguous() or tuple(sw.shape) != (G, (N + 127) // 128, K // 128):
+        raise ValueError("sw must be a contiguous [G, ceil(N/128), K/128] tensor")
+    if offsets.dtype != torch.int32 or offsets.numel() != G + 1:
+        raise ValueError("offsets must be int32 [G+1]")
+    if c is None:
+        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    st = _lib.fp8_grouped_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(w),
+                               w.stride(1), _ptr(sw), _ptr(offsets), G, M, _ptr(c),
+                               _out_code(c.dtype), c.stride(0), N, K, _stream(a))
+    _check(st, "fp8_grouped_gemm")
+    return c

@@ -1,0 +1,75 @@
+"""Shared helpers for the GPU parity tests: host <-> device marshalling, the
+seeded output-element samples, and the comparison against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+
+def to_dev(x: np.ndarray, dev="cuda") -> torch.Tensor:
+    """float32 arrays become float32 tensors; uint16 arrays are BF16 bits."""
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+def codes(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def scale_bits(t: torch.Tensor) -> np.ndarray:
+    return np.ascontiguousarray(t.cpu().numpy()).view(np.uint32)
+
+
+def assert_same_bytes(gpu: np.ndarray, ref: np.ndarray, what: str):
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    if not np.array_equal(gpu, ref):
+        bad = np.argwhere(gpu != ref)
+        i = tuple(bad[0])
+        raise AssertionError(f"{what}: {len(bad)} mismatches, first at {i}: gpu {gpu[i]!r} "
+                             f"oracle {ref[i]!r}")
+
+
+def sample_elements(M: int, N: int, seed: int, rows: int = 16, cols: int = 16,
+                    rand: int = 4096, block: int = 128):
+    """Seeded output sample: `rows` full rows, `cols` full columns, `rand`
+    random elements, and every element of the first and last block x block
+    output tiles (which carry the M and N tails)."""
+    rng = np.random.default_rng(seed)
+    ms, ns = [], []
+    for m in rng.choice(M, size=min(rows, M), replace=False):
+        ms.append(np.full(N, m))
+        ns.append(np.arange(N))
+    for n in rng.choice(N, size=min(cols, N), replace=False):
+        ms.append(np.arange(M))
+        ns.append(np.full(M, n))
+    ms.append(rng.integers(0, M, rand))
+    ns.append(rng.integers(0, N, rand))
+    for m0, n0 in ((0, 0), ((M - 1) // block * block, (N - 1) // block * block)):
+        mm, nn = np.meshgrid(np.arange(m0, min(M, m0 + block)), np.arange(n0, min(N, n0 + block)),
+                             indexing="ij")
+        ms.append(mm.ravel())
+        ns.append(nn.ravel())
+    mi = np.concatenate(ms).astype(np.int64)
+    ni = np.concatenate(ns).astype(np.int64)
+    key = np.unique(mi * N + ni)
+    return key // N, key % N
+
+
+def check_gemm(c_gpu: np.ndarray, c_ref: np.ndarray, s_ref: np.ndarray, bf16_out: bool,
+               what: str) -> float:
+    """|gpu - C*| <= 1e-3 * S (+ one BF16 ulp of C* for BF16 output), all
+    finite.  Returns max |err| / (1e-3 * S) over elements with S > 0."""
+    from oracle import oracle
+    g = np.asarray(c_gpu, dtype=np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    tol = oracle.gemm_tolerance(c_ref, s_ref, bf16_out)
+    err = np.abs(g - c_ref)
+    bad = err > tol
+    if bad.any():
+        i = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError(f"{what}: {int(bad.sum())} elements out of tolerance; first flat "
+                             f"index {i}: gpu {g.ravel()[i]!r} exact {c_ref.ravel()[i]!r} "
+                             f"tol {tol.ravel()[i]!r}")
+    rel = err / np.where(s_ref > 0, 1e-3 * s_ref, np.inf)
+    return float(rel.max()) if rel.size else 0.0

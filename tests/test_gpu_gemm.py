@@ -1,0 +1,176 @@
+"""GPU parity of the block-scaled FP8 GEMM against the oracle's exact
+per-K-block value: |gpu - C*| <= 1e-3 * sum|a*b| (FP32 output), plus one
+BF16 ulp of C* for BF16 output; no NaN or Inf.  The promotion of every
+128-wide K interval with both block scales is the jp-study.kr page's
+Figure 7(b); the Fprop, Dgrad and Wgrad shapes are Figure 6's linear-layer
+GEMMs.
+
+The oracle always quantizes the synthetic inputs itself; the GPU side uses
+the GPU quantizers (whose bit-exactness is tested separately)."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_quant_amd import synth
+from helpers import check_gemm, sample_elements, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import fp8_fine_grained_quant_amd as fq
+    return fq
+
+
+def _rand_scaled(rng, shape, spread=3.0):
+    return (rng.standard_normal(shape) * np.exp(rng.uniform(-spread, spread, (shape[0], 1)))).astype(
+        np.float32)
+
+
+def _full_check(fq, oracle, a, w, out_dtype, what):
+    """Quantize a (1x128) and w (128x128) on both sides; compare all of C."""
+    qa_o, sa_o = oracle.quant_1x128(a)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qw_o, sw_o)
+    qa, sa = fq.fp8_quant_1x128(to_dev(a))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    c = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return check_gemm(c.float().cpu().numpy(), c_ref, s_ref, out_dtype == torch.bfloat16, what)
+
+
+def test_gemm_tiny_config_bf16(fq, oracle):
+    a, w = synth.tiny_inputs()
+    r = _full_check(fq, oracle, a, w, torch.bfloat16, "tiny fprop bf16")
+    print(f"tiny: max |err| / (1e-3 sum|ab|) = {r:.3g}")
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 300, 256), (300, 200, 384), (256, 256, 128),
+                                   (257, 513, 256), (512, 768, 1024), (33, 1000, 640),
+                                   (1000, 40, 512)])
+def test_gemm_shapes_and_tails(fq, oracle, M, N, K, out):
+    rng = np.random.default_rng(M * 7 + N * 13 + K)
+    a = _rand_scaled(rng, (M, K))
+    w = _rand_scaled(rng, (N, K), 1.0) * np.float32(0.05)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    _full_check(fq, oracle, a, w, dt, f"{M}x{N}x{K} {out}")
+
+
+def test_gemm_row128_scales(fq, oracle):
+    """ROW128: B carries one scale per row per 128 K (the weight-gradient
+    layout, both operands quantized along the reduction dimension)."""
+    rng = np.random.default_rng(21)
+    T, M, N = 640, 300, 520                 # reduction over T tokens
+    dy = _rand_scaled(rng, (T, M))
+    x = _rand_scaled(rng, (T, N))
+    qa_o, sa_o = oracle.quant_1x128(dy, transposed=True)     # dY^T [M, T]
+    qb_o, sb_o = oracle.quant_1x128(x, transposed=True)      # X^T  [N, T]
+    c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qb_o, sb_o, mode=oracle.SCALE_ROW128)
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy), transposed=True)
+    qb, sb = fq.fp8_quant_1x128(to_dev(x), transposed=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qb, sb, out_dtype=torch.float32,
+                                scale_mode=fq.SCALE_ROW128)
+    torch.cuda.synchronize()
+    check_gemm(c.cpu().numpy(), c_ref, s_ref, False, "row128")
+
+
+def test_gemm_transposed_weight_scales(fq, oracle):
+    """Input-gradient shape: B = W^T codes from the 128x128 quantizer's
+    transposed copy, its block scales read transposed through strides."""
+    rng = np.random.default_rng(22)
+    M, Nw, Kw = 384, 640, 384                # dX[M, Kw] = dY[M, Nw] * W[Nw, Kw]
+    dy = _rand_scaled(rng, (M, Nw))
+    w = _rand_scaled(rng, (Nw, Kw), 1.0) * np.float32(0.02)
+    qa_o, sa_o = oracle.quant_1x128(dy)
+    _, sw_o, qwt_o = oracle.quant_128x128(w, with_transpose=True)
+    c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qwt_o, sw_o, sbs=(1, sw_o.shape[1]))
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy))
+    _, sw, qwt = fq.fp8_quant_128x128(to_dev(w), with_transpose=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qwt, sw.t(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_gemm(c.cpu().numpy(), c_ref, s_ref, False, "dgrad-style")
+
+
+def test_gemm_padding_untouched_and_repeatable(fq, oracle):
+    rng = np.random.default_rng(23)
+    M, N, K = 300, 260, 512
+    a = _rand_scaled(rng, (M, K))
+    w = _rand_scaled(rng, (N, K))
+    qa, sa = fq.fp8_quant_1x128(to_dev(a))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    cbuf = torch.full((M, 272), float("nan"), dtype=torch.float32, device="cuda")
+    c1 = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=torch.float32, c=cbuf[:, :N])
+    torch.cuda.synchronize()
+    assert torch.isnan(cbuf[:, N:]).all(), "ldc padding was written"
+    c2 = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=torch.float32)
+    assert torch.equal(c1.view(torch.int32), c2.view(torch.int32)), "not bitwise repeatable"
+    qa_o, sa_o = oracle.quant_1x128(a)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qw_o, sw_o)
+    check_gemm(c2.cpu().numpy(), c_ref, s_ref, False, "padded")
+
+
+def test_gemm_zero_groups_and_extreme_scales(fq, oracle):
+    """All-zero K blocks (scale +0) and activations spanning ~2^+-40 in one
+    row: the promotion must not produce NaN/Inf and stays within tolerance."""
+    rng = np.random.default_rng(24)
+    M, N, K = 256, 256, 768
+    a = rng.standard_normal((M, K)).astype(np.float32)
+    a[:, 128:256] = 0.0
+    a[:8] *= np.float32(2.0 ** 40)
+    a[8:16] *= np.float32(2.0 ** -40)
+    w = rng.standard_normal((N, K)).astype(np.float32)
+    w[:128, 512:640] = 0.0
+    _full_check(fq, oracle, a, w, torch.float32, "zero groups")
+
+
+# --- the large configurations, on sampled outputs -------------------------------
+
+def _sampled_check(fq, oracle, qa_o, sa_o, qb_o, sb_o, c, mode, sbs, bf16_out, seed, what):
+    M, N = c.shape
+    mi, ni = sample_elements(M, N, seed)
+    c_ref, s_ref = oracle.gemm_exact_elems(qa_o, sa_o, qb_o, sb_o, mi, ni, mode=mode, sbs=sbs)
+    cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    assert torch.isfinite(c.float()).all(), f"{what}: non-finite output"
+    r = check_gemm(cg, c_ref, s_ref, bf16_out, what)
+    print(f"{what}: {mi.size} sampled elements, max |err| / (1e-3 sum|ab|) = {r:.3g}")
+
+
+def test_gemm_fprop_large(fq, oracle):
+    a, w = synth.fprop_inputs()
+    qa_o, sa_o = oracle.quant_1x128(a)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    qa, sa = fq.fp8_quant_1x128(to_dev(a))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    c = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _sampled_check(fq, oracle, qa_o, sa_o, qw_o, sw_o, c, oracle.SCALE_BLOCK128, None, True, 2,
+                   "fprop 8192x18432x7168 bf16")
+
+
+def test_gemm_dgrad_large(fq, oracle):
+    dy, w = synth.dgrad_inputs()
+    qa_o, sa_o = oracle.quant_1x128(dy)
+    _, sw_o, qwt_o = oracle.quant_128x128(w, with_transpose=True)
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy))
+    _, sw, qwt = fq.fp8_quant_128x128(to_dev(w), with_transpose=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qwt, sw.t(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    _sampled_check(fq, oracle, qa_o, sa_o, qwt_o, sw_o, c, oracle.SCALE_BLOCK128,
+                   (1, sw_o.shape[1]), False, 3, "dgrad 8192x7168x18432 f32")
+
+
+def test_gemm_wgrad_large(fq, oracle):
+    dy, x = synth.wgrad_inputs()
+    qa_o, sa_o = oracle.quant_1x128(dy, transposed=True)
+    qb_o, sb_o = oracle.quant_1x128(x, transposed=True)
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy), transposed=True)
+    qb, sb = fq.fp8_quant_1x128(to_dev(x), transposed=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qb, sb, out_dtype=torch.float32,
+                                scale_mode=fq.SCALE_ROW128)
+    torch.cuda.synchronize()
+    _sampled_check(fq, oracle, qa_o, sa_o, qb_o, sb_o, c, oracle.SCALE_ROW128, None, False, 4,
+                   "wgrad 2048x7168x8192 f32")

@@ -1,0 +1,127 @@
+"""GPU parity of the grouped (MoE expert) GEMM: the forward GEMM of the MoE
+up-projection on activations quantized before dispatch (jp-study.kr page,
+passage on FP8 dispatch and the up-projection), with per-expert 128x128 weight
+scales.  Tolerance as for the dense GEMM."""
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_quant_amd import synth
+from helpers import assert_same_bytes, check_gemm, codes, scale_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import fp8_fine_grained_quant_amd as fq
+    return fq
+
+
+def _offsets(counts):
+    off = np.zeros(len(counts) + 1, dtype=np.int32)
+    off[1:] = np.cumsum(counts)
+    return off
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("counts,N,K", [([0, 300, 1, 0, 257, 128], 384, 256),
+                                        ([5], 256, 128),
+                                        ([0, 0, 513], 200, 384),
+                                        ([1] * 40, 256, 256)])
+def test_grouped_small_full(fq, oracle, counts, N, K, out):
+    rng = np.random.default_rng(len(counts) * 100 + N + K)
+    off = _offsets(counts)
+    Mt, G = int(off[-1]), len(counts)
+    x = (rng.standard_normal((Mt, K)) * np.exp(rng.uniform(-3, 3, (Mt, 1)))).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)
+    qa_o, sa_o = oracle.quant_1x128(x)
+    qw_o, sw_o, _ = oracle.quant_128x128(w.reshape(G * N, K))
+    gn = (N + 127) // 128
+    qw_o = qw_o.reshape(G, N, K)
+    sw_o = sw_o.reshape(G, gn, K // 128) if N % 128 == 0 else None
+    if sw_o is None:   # blocks straddle groups when N % 128 != 0: quantize per group
+        qs = [oracle.quant_128x128(w[g]) for g in range(G)]
+        qw_o = np.stack([q for q, _, _ in qs])
+        sw_o = np.stack([s for _, s, _ in qs])
+    mi, ni = np.meshgrid(np.arange(Mt), np.arange(N), indexing="ij")
+    c_ref, s_ref = oracle.grouped_gemm_exact_elems(qa_o, sa_o, qw_o, sw_o, off, mi.ravel(),
+                                                   ni.ravel())
+    qa, sa = fq.fp8_quant_1x128(to_dev(x))
+    wd = to_dev(w)
+    qw = torch.empty((G, N, K), dtype=torch.uint8, device="cuda")
+    sw = torch.empty((G, gn, K // 128), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        fq.fp8_quant_128x128(wd[g], q=qw[g], s=sw[g])
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = fq.fp8_grouped_gemm(qa, sa, qw, sw, torch.from_numpy(off).cuda(), out_dtype=dt)
+    torch.cuda.synchronize()
+    assert_same_bytes(codes(qw), qw_o, "expert weight codes")
+    check_gemm(c.float().cpu().numpy().ravel(), c_ref, s_ref, out == "bf16", f"grouped {counts}")
+
+
+def test_grouped_moe_config(fq, oracle):
+    """256 experts, 32768 tokens x top-8 (Zipf 1.1 popularity, 4 experts
+    forced empty), X_g[262144,7168] * W_e[2048,7168]^T, BF16 out.  Checked:
+    the 1x128 codes/scales of every grouped row (via the gather identity
+    quant(gather(X)) == gather(quant(X))), the 128x128 codes/scales of two
+    128-row blocks of every expert, and C on the first, last and two random
+    rows of every non-empty expert at 10 columns of those blocks."""
+    rt = synth.moe_routing_default()
+    E, N, K = synth.MOE_EXPERTS, 2048, 7168
+    off = rt.offsets
+    Mt = int(off[-1])
+    print(f"moe: {Mt} rows, {int((rt.counts == 0).sum())} empty experts, max {rt.counts.max()}",
+          flush=True)
+    xtok = synth.moe_tokens()
+    w = synth.moe_expert_weights(range(E))                    # [E, N, K] bf16 bits
+    # device side: gather, quantize, GEMM
+    xg = to_dev(xtok)[torch.from_numpy(rt.token_of_row).cuda()]
+    qa, sa = fq.fp8_quant_1x128(xg)
+    del xg
+    wd = to_dev(w.reshape(E * N, K))
+    qw, sw, _ = fq.fp8_quant_128x128(wd)
+    del wd
+    c = fq.fp8_grouped_gemm(qa, sa, qw.view(E, N, K), sw.view(E, N // 128, K // 128),
+                            torch.from_numpy(off).cuda(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    print("moe: gpu done", flush=True)
+    # activations: oracle quantizes the 32768 token rows, rows are gathered
+    qt_o, st_o = oracle.quant_1x128(xtok)
+    assert_same_bytes(codes(qa), qt_o[rt.token_of_row], "grouped activation codes")
+    assert_same_bytes(scale_bits(sa), st_o[:, rt.token_of_row].view(np.uint32),
+                      "grouped activation scales")
+    # weights: two 128-row blocks per expert
+    rng = np.random.default_rng(55)
+    blocks = [(e, 0) for e in range(E)] + [(e, int(rng.integers(1, N // 128))) for e in range(E)]
+    qw_h = codes(qw).reshape(E, N, K)
+    sw_h = scale_bits(sw).reshape(E, N // 128, K // 128)
+    qw_o = np.zeros((E, N, K), dtype=np.uint8)
+    sw_o = np.zeros((E, N // 128, K // 128), dtype=np.float32)
+    for e, b in blocks:
+        q, s, _ = oracle.quant_128x128(w[e, b * 128:(b + 1) * 128])
+        qw_o[e, b * 128:(b + 1) * 128] = q
+        sw_o[e, b] = s[0]
+        assert_same_bytes(qw_h[e, b * 128:(b + 1) * 128], q, f"expert {e} block {b} codes")
+        assert_same_bytes(sw_h[e, b], s[0].view(np.uint32), f"expert {e} block {b} scales")
+    # GEMM sample
+    ms, ns = [], []
+    for e in range(E):
+        if rt.counts[e] == 0:
+            continue
+        rows = [off[e], off[e + 1] - 1] + list(rng.integers(off[e], off[e + 1], 2))
+        cols = [0, 127] + list(rng.integers(0, 128, 3))
+        bb = [b for ee, b in blocks if ee == e and b != 0][0]
+        cols += [bb * 128, bb * 128 + 127] + list(bb * 128 + rng.integers(0, 128, 3))
+        for r in rows:
+            for cc in cols:
+                ms.append(r)
+                ns.append(cc)
+    mi = np.array(ms, dtype=np.int64)
+    ni = np.array(ns, dtype=np.int64)
+    c_ref, s_ref = oracle.grouped_gemm_exact_elems(qt_o[rt.token_of_row], st_o[:, rt.token_of_row],
+                                                   qw_o, sw_o, off, mi, ni)
+    cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, True, "moe grouped")
+    print(f"moe: {mi.size} sampled elements, max |err| / (1e-3 sum|ab|) = {r:.3g}")

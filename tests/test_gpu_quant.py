@@ -1,0 +1,174 @@
+"""GPU parity of the quantizers: every code byte and every FP32 scale bit
+pattern must equal the CPU oracle's (1x128 activation tiles and 128x128
+weight blocks, "Should Fixing Deepseek Take 60 Steps?", Figure 7(a); 128x1
+groups along tokens for the weight-gradient GEMM)."""
+import concurrent.futures as cf
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from fp8_fine_grained_quant_amd import synth
+from helpers import assert_same_bytes, codes, scale_bits, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fq():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    import fp8_fine_grained_quant_amd as fq
+    return fq
+
+
+def _check_1x128(fq, oracle, x, transposed=False, what=""):
+    q, s = fq.fp8_quant_1x128(to_dev(x), transposed=transposed)
+    qo, so = oracle.quant_1x128(x, transposed=transposed)
+    torch.cuda.synchronize()
+    assert_same_bytes(codes(q), qo, what + " codes")
+    assert_same_bytes(scale_bits(s), so.view(np.uint32), what + " scales")
+
+
+def test_quant_1x128_tiny_f32(fq, oracle):
+    a, _ = synth.tiny_inputs()
+    _check_1x128(fq, oracle, a, what="A[256,512] f32")
+
+
+def test_quant_1x128_fprop_activation(fq, oracle):
+    a, _ = synth.fprop_inputs(n=128)            # A[8192,7168] bf16 with outliers (W unused)
+    _check_1x128(fq, oracle, a, what="A[8192,7168] bf16")
+
+
+def test_quant_1x128_dgrad_output_grad(fq, oracle):
+    dy = synth.f32_to_bf16_bits(synth.normal_f32((8192, 18432), 1e-3, 301))
+    _check_1x128(fq, oracle, dy, what="dY[8192,18432] bf16")
+
+
+def test_quant_128x1_wgrad_operands(fq, oracle):
+    dy, x = synth.wgrad_inputs()
+    _check_1x128(fq, oracle, dy, transposed=True, what="dY^T 128x1")
+    _check_1x128(fq, oracle, x, transposed=True, what="X^T 128x1")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1), (3, 7), (37, 300), (129, 128), (5, 1000), (260, 136)])
+def test_quant_1x128_ragged(fq, oracle, dtype, shape):
+    rng = np.random.default_rng(shape[0] * 1000 + shape[1])
+    x = (rng.standard_normal(shape) * np.exp(rng.uniform(-5, 5, (shape[0], 1)))).astype(np.float32)
+    if dtype == "bf16":
+        x = synth.f32_to_bf16_bits(x)
+    _check_1x128(fq, oracle, x, what=f"{shape} {dtype}")
+    _check_1x128(fq, oracle, x, transposed=True, what=f"{shape} {dtype} transposed")
+
+
+def test_quant_1x128_padded_leading_dims_untouched(fq, oracle):
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((40, 384)).astype(np.float32)
+    xd = torch.zeros((40, 520), dtype=torch.float32, device="cuda")
+    xd[:, :384] = to_dev(x)
+    q = torch.full((40, 400), 0xA5, dtype=torch.uint8, device="cuda")
+    s = torch.full((3, 48), float("nan"), dtype=torch.float32, device="cuda")
+    fq.fp8_quant_1x128(xd[:, :384], q=q[:, :384], s=s[:, :40])
+    qo, so = oracle.quant_1x128(x)
+    assert_same_bytes(codes(q)[:, :384], qo, "codes")
+    assert np.all(codes(q)[:, 384:] == 0xA5), "row padding of q was written"
+    assert_same_bytes(scale_bits(s)[:, :40], so.view(np.uint32), "scales")
+    assert torch.isnan(s[:, 40:]).all(), "padding of s was written"
+
+
+def test_quant_1x128_special_groups(fq, oracle):
+    x = np.zeros((8, 512), dtype=np.float32)
+    x[1, :128] = -0.0                                  # all negative zero
+    x[2, 128:256] = 1e-40                              # FP32 subnormal amax
+    x[2, 130] = -3e-41
+    x[3, 256:384] = np.float32(3.0e38)                 # near FLT_MAX
+    x[3, 300] = -np.float32(3.4e38)
+    x[4, :] = np.float32(448.0)
+    x[4, 1::2] = -np.float32(447.99997)
+    x[5, :] = np.linspace(-2.0 ** -10, 2.0 ** -10, 512, dtype=np.float32)
+    x[6, :] = np.float32(1e-37)                        # 448/amax overflows to +inf -> FLT_MAX
+    x[6, 7] = 5e-38
+    x[7, :] = np.float32(3.2e-43)                      # amax/448 is the smallest subnormal
+    _check_1x128(fq, oracle, x, what="special groups")
+    _check_1x128(fq, oracle, np.ascontiguousarray(x[:, :256].T.copy()), transposed=True,
+                 what="special groups transposed")
+
+
+def _check_128x128(fq, oracle, w, with_t, what):
+    q, s, qt = fq.fp8_quant_128x128(to_dev(w), with_transpose=with_t)
+    qo, so, qto = oracle.quant_128x128(w, with_transpose=with_t)
+    torch.cuda.synchronize()
+    assert_same_bytes(codes(q), qo, what + " codes")
+    assert_same_bytes(scale_bits(s), so.view(np.uint32), what + " scales")
+    if with_t:
+        assert_same_bytes(codes(qt), qto, what + " transposed codes")
+
+
+def test_quant_128x128_tiny_f32(fq, oracle):
+    _, w = synth.tiny_inputs()
+    _check_128x128(fq, oracle, w, True, "W[256,512] f32")
+
+
+def test_quant_128x128_fprop_weight(fq, oracle):
+    w = synth.f32_to_bf16_bits(synth.normal_f32((18432, 7168), 0.02, 202))
+    _check_128x128(fq, oracle, w, True, "W[18432,7168] bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1), (7, 3), (300, 200), (128, 136), (257, 1000)])
+def test_quant_128x128_ragged(fq, oracle, dtype, shape):
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    w = rng.standard_normal(shape).astype(np.float32)
+    if dtype == "bf16":
+        w = synth.f32_to_bf16_bits(w)
+    _check_128x128(fq, oracle, w, True, f"{shape} {dtype}")
+
+
+def test_quant_repeatable(fq):
+    a, _ = synth.fprop_inputs(m=2048, n=128)
+    xd = to_dev(a)
+    q1, s1 = fq.fp8_quant_1x128(xd)
+    q2, s2 = fq.fp8_quant_1x128(xd)
+    assert torch.equal(q1, q2) and torch.equal(s1.view(torch.int32), s2.view(torch.int32))
+
+
+def _encode_chunk_expected(oracle, bits: np.ndarray) -> np.ndarray:
+    parts = np.array_split(bits, 8)
+    with cf.ThreadPoolExecutor(8) as ex:
+        outs = list(ex.map(lambda b: oracle.e4m3_encode(b.view(np.float32)), parts))
+    return np.concatenate(outs)
+
+
+def test_encode_every_fp32_pattern_up_to_448(fq, oracle):
+    """Every FP32 bit pattern with |v| <= 448, through the public quantizer:
+    each 1x128 group holds 448 (so inv = 448/448 = 1 and x*inv = x exactly)
+    and 127 patterns; their codes must equal the oracle's encoder."""
+    top = int(np.array([448.0], np.float32).view(np.uint32)[0])      # 0x43E00000
+    chunk = 127 * (1 << 19)
+    starts = list(range(0, top + 1, chunk))
+    done = 0
+    for sign in (0, 0x80000000):
+        for st in starts:
+            n = min(chunk, top + 1 - st)
+            ngroups = (n + 126) // 127
+            pat = torch.arange(st, st + n, dtype=torch.int64, device="cuda")
+            pat = (pat | sign).to(torch.int64)
+            pat32 = (pat - (1 << 32) * (pat >= (1 << 31))).to(torch.int32)
+            xs = torch.zeros((ngroups, 128), dtype=torch.float32, device="cuda")
+            xs[:, 0] = 448.0
+            flat = xs[:, 1:].reshape(-1)
+            flat[:n] = pat32.view(torch.float32)
+            xs[:, 1:] = flat.view(ngroups, 127)
+            q, s = fq.fp8_quant_1x128(xs)
+            got = q[:, 1:].reshape(-1)[:n].cpu().numpy()
+            assert torch.all(s == 1.0)
+            bits = (np.arange(st, st + n, dtype=np.uint64) | sign).astype(np.uint32)
+            exp = _encode_chunk_expected(oracle, bits)
+            if not np.array_equal(got, exp):
+                i = np.flatnonzero(got != exp)[0]
+                v = bits[i:i + 1].view(np.float32)[0]
+                raise AssertionError(f"pattern {bits[i]:#010x} ({v!r}): gpu {got[i]:#04x} "
+                                     f"oracle {exp[i]:#04x}")
+            done += n
+    assert done == 2 * (top + 1)
