@@ -163,6 +163,15 @@ def _out_code(dtype) -> int:
     raise TypeError("output dtype must be bfloat16 or float32")
 
 
+def _alloc_out(M: int, N: int, dtype, device) -> torch.Tensor:
+    """Output [M, N] whose row pitch is a multiple of 4 elements (the GEMM
+    stores 4 consecutive columns per lane); a view of a padded buffer when N
+    is not."""
+    ld = (N + 3) // 4 * 4
+    buf = torch.empty((M, ld), dtype=dtype, device=device)
+    return buf if ld == N else buf[:, :N]
+
+
 def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
                          out_dtype=torch.bfloat16, scale_mode: int = SCALE_BLOCK128,
                          c: torch.Tensor | None = None):
@@ -186,7 +195,7 @@ def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb:
             raise ValueError("ROW128 sb must be contiguous along dim 1")
         sbs0, sbs1 = sb.stride(0), 0
     if c is None:
-        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+        c = _alloc_out(M, N, out_dtype, a.device)
     _require_cuda(c)
     if c.stride(1) != 1:
         raise ValueError("c must be contiguous along dim 1")
@@ -215,7 +224,7 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: tor
     if offsets.dtype != torch.int32 or offsets.numel() != G + 1:
         raise ValueError("offsets must be int32 [G+1]")
     if c is None:
-        c = torch.empty((M, N), dtype=out_dtype, device=a.device)
+        c = _alloc_out(M, N, out_dtype, a.device)
     st = _lib.fp8_grouped_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(w),
                                w.stride(1), _ptr(sw), _ptr(offsets), G, M, _ptr(c),
                                _out_code(c.dtype), c.stride(0), N, K, _stream(a))
