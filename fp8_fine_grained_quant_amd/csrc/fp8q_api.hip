@@ -82,6 +82,8 @@ int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, int64_t ld
         !aligned(sb, 4))
         return FP8Q_EALIGN;
     if (lda % 16 != 0 || ldb % 16 != 0 || ldc % 4 != 0) return FP8Q_EALIGN;
+    // the kernels address a 256-row tile with 32-bit byte offsets
+    if (lda > (int64_t(1) << 24) || ldb > (int64_t(1) << 24)) return FP8Q_EUNSUPPORTED;
     return FP8Q_OK;
 }
 
@@ -102,6 +104,8 @@ FP8Q_API int fp8_blockscaled_gemm(const uint8_t* a, int64_t lda, const float* sa
     if (st != FP8Q_OK) return st;
     if (sbs0 < 0 || sbs1 < 0) return FP8Q_EINVAL;
     if (b_scale_mode == FP8Q_SCALE_ROW128 && sbs0 < N) return FP8Q_EINVAL;
+    if (b_scale_mode == FP8Q_SCALE_BLOCK128 && ((N + 127) / 128) * sbs0 > (int64_t(1) << 29))
+        return FP8Q_EUNSUPPORTED;  // 32-bit byte offsets into sb
     // the tile grid is one workgroup per 256x256 output tile
     if ((M + 255) / 256 * ((N + 255) / 256) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
     fp8q::GemmParams p{};

@@ -21,9 +21,9 @@
 //    promotion FMA).
 //  * A and B K-slabs (256x128 bytes each) go HBM -> LDS with
 //    global_load_lds_dwordx4 (no VGPR staging), double buffered: the next
-//    slab streams in while the current one is multiplied.  LDS rows are
-//    128 bytes; 16-byte chunk c of row r is stored at slot c ^ (r & 7) so
-//    that the fragment reads (16 rows, same chunk) hit distinct banks.
+//    slab streams in while the current one is multiplied.  Rows are 128
+//    bytes with an XOR chunk swizzle that keeps both the copies (8 lanes per
+//    row) coalesced and the fragment reads free of bank conflicts (see swz).
 //  * Wave tile 64(M) x 128(N): 4 x 8 blocks of 16x16, 128 FP32 accumulator
 //    VGPRs.  The MFMA is issued with the B slab as its first operand, so a
 //    lane's four result registers are four CONSECUTIVE output columns of one
@@ -82,12 +82,26 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
     asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
 }
 
-__device__ __forceinline__ v8i frag32(const uint8_t* __restrict__ slab, int row, int kq) {
-    // 32 bytes of row `row` of a 128-byte-per-row swizzled slab: logical
-    // 16-byte chunks 2*kq and 2*kq+1 (stored at chunk ^ (row & 7)).
+// LDS layout of a 256-row x 128-byte operand slab: row r at r*128, its
+// 16-byte K chunk c at slot c ^ ((r >> 1) & 7).  The LDS returns 256 bytes
+// per clock to a 16-lane quarter of a ds_read_b128; a fragment read has the
+// 16 rows of a block in one quarter, all at the same logical chunk, and the
+// swizzle puts them in 16 distinct 16-byte bank groups (rows of equal
+// parity differ in (r >> 1) & 7, rows of opposite parity sit in opposite
+// 128-byte halves of the 256-byte bank window).  The copy side stays fully
+// coalesced: 8 consecutive lanes fetch one row's 128 bytes.
+// Lane l = 16*kq + r of a wave holds, for block b, row 16b + r, K chunks
+// 2kq and 2kq+1 (32 bytes).  The matrix instruction sums over its 128 K
+// positions in the same order for both operands, so any K assignment shared
+// by A and B gives the same dot products.
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+__device__ __forceinline__ v8i frag32(const uint8_t* __restrict__ slab, int block, int lane) {
+    const int row = block * 16 + (lane & 15);
+    const int kq = lane >> 4;
     const uint8_t* rb = slab + row * BK;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(rb + (((2 * kq) ^ (row & 7)) << 4));
-    const uint4 x1 = *reinterpret_cast<const uint4*>(rb + (((2 * kq + 1) ^ (row & 7)) << 4));
+    const uint4 x0 = *reinterpret_cast<const uint4*>(rb + (swz(row, 2 * kq) << 4));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(rb + (swz(row, 2 * kq + 1) << 4));
     return (v8i){(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w,
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
@@ -102,90 +116,49 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b) {
 struct LoadCtx {
     const uint8_t* a_base;  // A + m0*lda (wave-uniform)
     const uint8_t* b_base;  // B + n0*ldb (wave-uniform)
-    uint32_t a_off[4];      // per 8-row block: row*lda + swizzled chunk offset
+    uint32_t a_off[4];      // per copy instruction: row*lda + K byte offset
     uint32_t b_off[4];
     const float* s_base;    // scale row of K step 0 (sa, or sb in ROW128 mode)
     uint32_t s_off;         // this lane's element offset, in bytes
     int64_t s_kstride;      // scale elements per K step
 };
 
-// One K step: issue the HBM -> LDS copy of step kb+1 into `nxt_*` (when
-// `issue`), then multiply the operands of step kb held in `cur_*`.  The
-// restrict-qualified stage pointers let the compiler see that the copy in
-// flight never writes the stage being read, so it does not wait for it;
-// completion is awaited explicitly (vmcnt) before the next step's barrier.
-template <int SCALE_MODE>
-__device__ __forceinline__ void kstep(const uint8_t* __restrict__ cur_a,
-                                      const uint8_t* __restrict__ cur_b,
-                                      const float* __restrict__ cur_sa,
-                                      const float* __restrict__ cur_sb,
-                                      uint8_t* __restrict__ nxt_a, uint8_t* __restrict__ nxt_b,
-                                      float* __restrict__ nxt_s, bool issue, int64_t koff_next,
-                                      int kb_next, const LoadCtx& lc, int wave, int wm, int wn,
-                                      int lane, v4f (&acc)[4][8]) {
-    if (issue) {
-        const uint8_t* ab = lc.a_base + koff_next;
-        const uint8_t* bb = lc.b_base + koff_next;
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-            dma16(ab, lc.a_off[qd], lds_addr(nxt_a + (wave * 4 + qd) * 1024));
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd)
-            dma16(bb, lc.b_off[qd], lds_addr(nxt_b + (wave * 4 + qd) * 1024));
-        dma4(lc.s_base + (int64_t)kb_next * lc.s_kstride, lc.s_off,
-             lds_addr(nxt_s + (wave & 3) * 64));
-    }
-
-    const int r16 = lane & 15;
-    const int kq = lane >> 4;
-    v8i af[4];
-    float sc[4];
-    const float sbv = SCALE_MODE == kScaleBlock128 ? cur_sb[wn] : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = wm * kWaveM + i * 16 + r16;
-        af[i] = frag32(cur_a, row, kq);
-        sc[i] = cur_sa[row];
-        if (SCALE_MODE == kScaleBlock128) sc[i] *= sbv;
-    }
-    // Two partial-sum sets: the MFMAs of column block j run while the
-    // promotion FMAs of block j-1 retire.
-    v4f part[2][4];
-    v8i bf = frag32(cur_b, wn * kWaveN + r16, kq);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[0][i] = mfma_f8(bf, af[i]);
-#pragma unroll
-    for (int j = 1; j <= 8; ++j) {
-        const int cb = j & 1, pb = cb ^ 1;
-        if (j < 8) {
-            bf = frag32(cur_b, wn * kWaveN + j * 16 + r16, kq);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part[cb][i] = mfma_f8(bf, af[i]);
-        }
-        float4 sbq = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (SCALE_MODE == kScaleRow128)
-            sbq = *reinterpret_cast<const float4*>(&cur_sb[wn * kWaveN + (j - 1) * 16 + kq * 4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v4f& a = acc[i][j - 1];
-            const v4f& pp = part[pb][i];
-            if (SCALE_MODE == kScaleBlock128) {
-                a[0] = fmaf(pp[0], sc[i], a[0]);
-                a[1] = fmaf(pp[1], sc[i], a[1]);
-                a[2] = fmaf(pp[2], sc[i], a[2]);
-                a[3] = fmaf(pp[3], sc[i], a[3]);
-            } else {
-                a[0] = fmaf(pp[0], sc[i] * sbq.x, a[0]);
-                a[1] = fmaf(pp[1], sc[i] * sbq.y, a[1]);
-                a[2] = fmaf(pp[2], sc[i] * sbq.z, a[2]);
-                a[3] = fmaf(pp[3], sc[i] * sbq.w, a[3]);
-            }
-        }
-    }
+__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Barrier that publishes/releases a stage: this wave's own LDS reads and
+// copies are complete, then all waves meet.
+__device__ __forceinline__ void stage_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Copy instruction q (0..8) of one K step into an LDS stage: q < 4 moves
+// 8 rows of the A slab, 4 <= q < 8 8 rows of the B slab, q == 8 the scales.
+__device__ __forceinline__ void issue_copy(int q, const LoadCtx& lc, int64_t koff, int kb,
+                                           uint8_t* st_a, uint8_t* st_b, float* st_s,
+                                           int wave) {
+    if (q < 4)
+        dma16(lc.a_base + koff, lc.a_off[q], lds_addr(st_a + (wave * 4 + q) * 1024));
+    else if (q < 8)
+        dma16(lc.b_base + koff, lc.b_off[q - 4], lds_addr(st_b + (wave * 4 + q - 4) * 1024));
+    else
+        dma4(lc.s_base + (int64_t)kb * lc.s_kstride, lc.s_off, lds_addr(st_s + (wave & 3) * 64));
+}
+
+// Promotion of one 16x16 block: acc += partial * scale (ROW128: the scale of
+// each of the lane's four columns differs).
+template <int SCALE_MODE>
+__device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const float4& sbq) {
+    if (SCALE_MODE == kScaleBlock128) {
+        a[0] = fmaf(pp[0], sci, a[0]);
+        a[1] = fmaf(pp[1], sci, a[1]);
+        a[2] = fmaf(pp[2], sci, a[2]);
+        a[3] = fmaf(pp[3], sci, a[3]);
+    } else {
+        a[0] = fmaf(pp[0], sci * sbq.x, a[0]);
+        a[1] = fmaf(pp[1], sci * sbq.y, a[1]);
+        a[2] = fmaf(pp[2], sci * sbq.z, a[2]);
+        a[3] = fmaf(pp[3], sci * sbq.w, a[3]);
+    }
+}
 
 template <int SCALE_MODE, int OUT, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
@@ -271,26 +244,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int nkb = (int)(p.K / BK);
     const int64_t nb_last = (N + 127) / 128 - 1;
 
-    // Per-lane copy sources.  Instruction qd of wave w moves rows
-    // 8*(4w+qd) .. +7 of a slab; lane l carries row +l/8, stored 16-byte
-    // slot l%8, which holds logical chunk (l%8) ^ (row & 7).  Rows past the
-    // tile's end are clamped (their results are never stored).
+    // Per-lane copy sources, as 32-bit offsets from a wave-uniform base.
+    // Rows past the tile's end are clamped (their results are never stored).
     // Offsets stay below 2^32: a tile spans 256 rows of at most 2^24 bytes
     // each (the host rejects larger leading dimensions).
     m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)m0) |
          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)m0 >> 32)) << 32);
     LoadCtx lc;
     {
-        const int r_in = lane >> 3;
-        const int slot = lane & 7;
+        // copy instruction qd of wave w fills rows 8*(4w+qd) .. +7 of a slab:
+        // lane l carries row +l/8 and stores 16-byte slot l%8, which holds
+        // logical chunk swz(row, l%8)
         lc.a_base = uniform_ptr(p.a + m0 * p.lda);
         lc.b_base = uniform_ptr(bptr + n0 * p.ldb);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
-            const int row = (wave * 4 + qd) * 8 + r_in;
-            const uint32_t chunk = (uint32_t)((slot ^ (row & 7)) * 16);
-            lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + chunk;
-            lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + chunk;
+            const int row = (wave * 4 + qd) * 8 + (lane >> 3);
+            const uint32_t kbyte = (uint32_t)(swz(row, lane & 7) * 16);
+            lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + kbyte;
+            lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
         }
         if (SCALE_MODE == kScaleRow128 && wave >= 4) {
             lc.s_base = uniform_ptr(sbptr + n0);
@@ -317,31 +289,91 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
 
-
-    // prologue: step 0 into stage 0
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-        dma16(lc.a_base, lc.a_off[qd], lds_addr(smem_ab[0] + (wave * 4 + qd) * 1024));
-#pragma unroll
-    for (int qd = 0; qd < 4; ++qd)
-        dma16(lc.b_base, lc.b_off[qd], lds_addr(smem_ab[0] + kSlabBytes + (wave * 4 + qd) * 1024));
-    dma4(lc.s_base, lc.s_off, lds_addr(&smem_s[0][s_half] + (wave & 3) * 64));
-
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int st = kb & 1;
-        // this wave's copies of step kb have landed; after the barrier every
-        // wave's have, and every wave has finished reading stage st^1
-        wait_vm_all();
-        barrier();
-        kstep<SCALE_MODE>(smem_ab[st], smem_ab[st] + kSlabBytes, &smem_s[st][0], &smem_s[st][BM],
-                          smem_ab[st ^ 1], smem_ab[st ^ 1] + kSlabBytes, &smem_s[st ^ 1][s_half],
-                          kb + 1 < nkb, (int64_t)(kb + 1) * BK, kb + 1, lc, wave, wm, wn, lane,
-                          acc);
-    }
-
-    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 block ----
+    // Software pipeline over K steps, two LDS stages.  Step kb runs the
+    // MFMAs of column blocks 0..6, then (after its last LDS read of stage
+    // kb&1) meets the other waves at one barrier, after which stage kb&1 is
+    // free and stage (kb+1)&1 holds step kb+1.  The copy of step kb+2 into
+    // the freed stage and the fragment loads of step kb+1 are then issued
+    // while block 7's MFMAs and the last promotions of step kb run, so the
+    // matrix pipe does not drain at the barrier.
     const int r16 = lane & 15;
     const int kq = lane >> 4;
+    auto stage_a = [&](int st) { return smem_ab[st]; };
+    auto stage_b = [&](int st) { return smem_ab[st] + kSlabBytes; };
+    auto stage_s = [&](int st) { return &smem_s[st][s_half]; };
+    auto copy_step = [&](int kb, int st) {
+        const int kbc = kb < nkb ? kb : nkb - 1;   // past the end: harmless refill
+#pragma unroll
+        for (int q = 0; q < 9; ++q)
+            issue_copy(q, lc, (int64_t)kbc * BK, kbc, stage_a(st), stage_b(st), stage_s(st), wave);
+    };
+
+    v8i af[4], bf[3];
+    float sc[4];
+    auto load_step_frags = [&](int st) {
+        const uint8_t* sa_ = stage_a(st);
+        const uint8_t* sb_ = stage_b(st);
+        bf[0] = frag32(sb_, wn * 8 + 0, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
+        bf[1] = frag32(sb_, wn * 8 + 1, lane);
+        bf[2] = frag32(sb_, wn * 8 + 2, lane);
+        const float sbv = SCALE_MODE == kScaleBlock128 ? smem_s[st][BM + wn] : 1.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[i] = smem_s[st][wm * kWaveM + i * 16 + r16] * sbv;
+    };
+
+    copy_step(0, 0);
+    stage_barrier();
+    copy_step(1, 1);
+    load_step_frags(0);
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        const uint8_t* cb_ = stage_b(cur);
+        v4f part[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[0][i] = mfma_f8(bf[0], af[i]);
+        // ROW128: the four column scales of block j for this lane
+        auto row_scales = [&](int j) {
+            if (SCALE_MODE != kScaleRow128) return make_float4(1.f, 1.f, 1.f, 1.f);
+            return *reinterpret_cast<const float4*>(&smem_s[cur][BM + wn * kWaveN + j * 16 + kq * 4]);
+        };
+        // B fragments run two column blocks ahead of their MFMAs.
+#pragma unroll
+        for (int j = 1; j <= 6; ++j) {
+            if (j + 2 <= 7) bf[(j + 2) % 3] = frag32(cb_, wn * 8 + j + 2, lane);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[j & 1][i] = mfma_f8(bf[j % 3], af[i]);
+            const float4 sbq = row_scales(j - 1);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][j - 1], part[(j - 1) & 1][i], sc[i], sbq);
+            // one scheduling region per column block keeps the partial sums
+            // of at most two blocks alive
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float4 sbq6 = row_scales(6), sbq7 = row_scales(7);
+        // every LDS read of stage cur has been issued: release it, and make
+        // step kb+1 (copied into cur^1 during the previous step) visible
+        stage_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        v4f last[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) last[i] = mfma_f8(bf[7 % 3], af[i]);
+        float sc_old[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc_old[i] = sc[i];
+        copy_step(kb + 2, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        load_step_frags(cur ^ 1);   // after the last step: unused, harmless reads
+#pragma unroll
+        for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][6], part[0][i], sc_old[i], sbq6);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][7], last[i], sc_old[i], sbq7);
+    }
+    wait_vm_all();
+
+    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 block ----
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + wm * kWaveM + i * 16 + r16;

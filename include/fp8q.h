@@ -138,6 +138,7 @@ int fp8_quant_128x128(const void* w, int w_dtype, int64_t rows, int64_t cols,
  *   c  : output, c[m*ldc + n], element type c_dtype (FP8Q_BF16: round to
  *        nearest even; FP8Q_F32); ldc >= N and a multiple of 4; 16-B aligned.
  *   K  : a positive multiple of 128, else FP8Q_EUNSUPPORTED.
+ * lda and ldb above 2^24 bytes return FP8Q_EUNSUPPORTED.
  * For every element: acc = sum over kb of (sa[m,kb]*sb[n,kb]) * P_kb, where
  * P_kb is the FP32 partial sum of the 128 products of the K block.
  */
