@@ -348,6 +348,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             const float4 sbq = row_scales(j - 1);
 #pragma unroll
             for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][j - 1], part[(j - 1) & 1][i], sc[i], sbq);
+            // issue order inside the block: MFMA, 4 promotion FMAs, with the
+            // two fragment reads of block j+2 slotted after the first two
+            // MFMAs -- the other wave of the SIMD fills the MFMA shadow
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                if (q < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+            }
             // one scheduling region per column block keeps the partial sums
             // of at most two blocks alive
             __builtin_amdgcn_sched_barrier(0);
