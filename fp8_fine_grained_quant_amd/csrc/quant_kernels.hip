@@ -29,9 +29,30 @@
 
 namespace fp8q {
 
+#ifndef FP8Q_ROW_UNROLL
+#define FP8Q_ROW_UNROLL 4
+#endif
+constexpr int kRowUnroll = FP8Q_ROW_UNROLL;
+
 // ---------------------------------------------------------------------------
 // 1x128 groups along contiguous rows
 // ---------------------------------------------------------------------------
+
+#ifndef FP8Q_NT
+#define FP8Q_NT 1
+#endif
+// Streaming 16-byte load: every input byte is read exactly once, so the
+// non-temporal hint keeps it from displacing reusable cache lines.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+#if FP8Q_NT
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#endif
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // Loads the 8 elements [c0, c0+8) of a row as FP32; elements at or beyond
 // `cols` read as 0 (they do not change the group max and are not stored).
@@ -41,7 +62,7 @@ __device__ __forceinline__ void load8(const void* row, int64_t c0, int64_t cols,
                                       bool vec) {
     if (vec && c0 + 8 <= cols) {
         if (DT == kBF16) {
-            uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + c0);
+            uint4 u = ld_stream16(static_cast<const uint16_t*>(row) + c0);
             uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -49,10 +70,12 @@ __device__ __forceinline__ void load8(const void* row, int64_t c0, int64_t cols,
                 v[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
             }
         } else {
-            const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + c0);
-            float4 a = p[0], b = p[1];
-            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+            const float* p = static_cast<const float*>(row) + c0;
+            const uint4 a = ld_stream16(p), b = ld_stream16(p + 4);
+            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
+            v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
+            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
+            v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
         }
     } else {
 #pragma unroll
@@ -69,11 +92,22 @@ __device__ __forceinline__ void load8(const void* row, int64_t c0, int64_t cols,
 }
 
 // Stores the 8 code bytes of [c0, c0+8) (those below `cols`); `vec`: the
-// row start is 8-byte aligned, so full runs use one 8-byte store.
+// row start is 8-byte aligned, so full runs use one 8-byte store.  STREAM:
+// non-temporal store, for outputs written in whole contiguous runs (the
+// transposed outputs are written 8 bytes per row and are better merged in
+// the cache first).
+template <bool STREAM = true>
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c0, int64_t cols, uint32_t lo,
                                        uint32_t hi, bool vec) {
     if (vec && c0 + 8 <= cols) {
+#if FP8Q_NT
+        if (STREAM)
+            __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(row + c0));
+        else
+            *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
+#else
         *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
+#endif
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -117,20 +151,21 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
     for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += (int64_t)gridDim.x * 4) {
         const void* xr = static_cast<const char*>(x) + (size_t)r * (size_t)ldx * esz;
         uint8_t* qr = q + r * ldq;
-        int64_t g = slice;
-        // two groups per trip so that two 16-byte loads are in flight per lane
-        for (; g + 4 < groups; g += 8) {
-            float v0[8], v1[8];
-            load8<DT>(xr, g * 128 + sl * 8, cols, v0, vin);
-            load8<DT>(xr, (g + 4) * 128 + sl * 8, cols, v1, vin);
-            quant_group_1x128<DT>(v0, qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0, vout);
-            quant_group_1x128<DT>(v1, qr, (g + 4) * 128 + sl * 8, cols, s + (g + 4) * lds + r,
-                                  sl == 0, vout);
-        }
-        if (g < groups) {
-            float v0[8];
-            load8<DT>(xr, g * 128 + sl * 8, cols, v0, vin);
-            quant_group_1x128<DT>(v0, qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0, vout);
+        // kRowUnroll group loads in flight per lane before any is consumed
+        for (int64_t g0 = 0; g0 < groups; g0 += 4 * kRowUnroll) {
+            float v[kRowUnroll][8];
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                const int64_t g = g0 + 4 * u + slice;
+                if (g < groups) load8<DT>(xr, g * 128 + sl * 8, cols, v[u], vin);
+            }
+#pragma unroll
+            for (int u = 0; u < kRowUnroll; ++u) {
+                const int64_t g = g0 + 4 * u + slice;
+                if (g < groups)
+                    quant_group_1x128<DT>(v[u], qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0,
+                                          vout);
+            }
         }
     }
 }
@@ -256,7 +291,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
                 tlo |= code_byte(lo[p], hi[p], j) << (8 * p);
                 thi |= code_byte(lo[p + 4], hi[p + 4], j) << (8 * p);
             }
-            if (c0 + j < cols) store8(qt + (c0 + j) * ldqt, r0, rows, tlo, thi, vqt);
+            if (c0 + j < cols) store8<false>(qt + (c0 + j) * ldqt, r0, rows, tlo, thi, vqt);
         }
     }
 }
