@@ -83,18 +83,23 @@ __device__ __forceinline__ void dma4(const void* base, uint32_t voff, uint32_t l
 }
 
 // LDS layout of a 256-row x 128-byte operand slab: row r at r*128, its
-// 16-byte K chunk c at slot c ^ ((r >> 1) & 7).  The LDS returns 256 bytes
-// per clock to a 16-lane quarter of a ds_read_b128; a fragment read has the
-// 16 rows of a block in one quarter, all at the same logical chunk, and the
-// swizzle puts them in 16 distinct 16-byte bank groups (rows of equal
-// parity differ in (r >> 1) & 7, rows of opposite parity sit in opposite
-// 128-byte halves of the 256-byte bank window).  The copy side stays fully
-// coalesced: 8 consecutive lanes fetch one row's 128 bytes.
+// 16-byte K chunk c at slot c ^ f(r) with f(r) = (r & 7) ^ ((r >> 3) & 1).
+// A fragment read (ds_read_b128) has the 16 rows of a block in one 16-lane
+// quarter of the wave, all at the same logical chunk.  f is a permutation
+// of 0..7 on rows 0..7 and on rows 8..15, and on each row-parity class of
+// the 16 rows (whose 128-byte rows fall alternately into the two halves of
+// a 256-byte bank window), so every 8-lane group and every 16-lane quarter
+// touches distinct banks: the read runs at the full LDS rate (measured with
+// the SQ_LDS_BANK_CONFLICT counter, zero conflict cycles, where f(r) =
+// (r >> 1) & 7 or f(r) = r & 7 alone cost two-way conflicts).  The copy side
+// stays fully coalesced: 8 consecutive lanes fetch one row's 128 bytes.
 // Lane l = 16*kq + r of a wave holds, for block b, row 16b + r, K chunks
 // 2kq and 2kq+1 (32 bytes).  The matrix instruction sums over its 128 K
 // positions in the same order for both operands, so any K assignment shared
 // by A and B gives the same dot products.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+}
 
 __device__ __forceinline__ v8i frag32(const uint8_t* __restrict__ slab, int block, int lane) {
     const int row = block * 16 + (lane & 15);
