@@ -9,7 +9,7 @@ loudly if it has not been built -- there is no fallback implementation.
 ``synth`` (seeded synthetic inputs) imports without the library.
 """
 _BINDINGS = ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_blockscaled_gemm",
-             "fp8_grouped_gemm", "fp8q_status_string", "library_path", "Fp8qError",
+             "fp8_grouped_gemm", "fp8_dispatch_rows", "fp8q_status_string", "library_path", "Fp8qError",
              "F32", "BF16", "SCALE_BLOCK128", "SCALE_ROW128")
 
 __all__ = list(_BINDINGS) + ["synth"]

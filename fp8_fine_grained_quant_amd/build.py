@@ -21,7 +21,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfp8q.so")
-SOURCES = ["fp8q_api.hip", "quant_kernels.hip", "gemm_kernels.hip"]
+SOURCES = ["fp8q_api.hip", "quant_kernels.hip", "gemm_kernels.hip", "dispatch_kernels.hip"]
 ARCH = "gfx950"
 
 

@@ -137,3 +137,22 @@ FP8Q_API int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, in
     p.offsets = offsets; p.num_groups = num_groups;
     return launch_status(fp8q::launch_grouped_gemm(p, c_dtype, stream));
 }
+
+FP8Q_API int fp8_dispatch_rows(const uint8_t* q_src, int64_t ldq_src, const float* s_src,
+                               int64_t lds_src, int64_t src_rows, const int32_t* index,
+                               int64_t rows, int64_t cols, uint8_t* q_dst, int64_t ldq_dst,
+                               float* s_dst, int64_t lds_dst, hipStream_t stream) {
+    if (rows < 0 || cols < 0 || src_rows < 0) return FP8Q_EINVAL;
+    if (rows == 0 || cols == 0) return FP8Q_OK;
+    if (!q_src || !s_src || !index || !q_dst || !s_dst) return FP8Q_EINVAL;
+    if (ldq_src < cols || ldq_dst < cols || lds_src < src_rows || lds_dst < rows)
+        return FP8Q_EINVAL;
+    if (!aligned(s_src, 4) || !aligned(s_dst, 4) || !aligned(index, 4)) return FP8Q_EALIGN;
+    if ((rows + 31) / 32 > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;  // grid size
+    fp8q::DispatchParams p{};
+    p.q_src = q_src; p.ldq_src = ldq_src; p.s_src = s_src; p.lds_src = lds_src;
+    p.src_rows = src_rows; p.index = index; p.rows = rows; p.cols = cols;
+    p.q_dst = q_dst; p.ldq_dst = ldq_dst; p.s_dst = s_dst; p.lds_dst = lds_dst;
+    p.vec = aligned(q_src, 16) && aligned(q_dst, 16) && ldq_src % 16 == 0 && ldq_dst % 16 == 0;
+    return launch_status(fp8q::launch_dispatch_rows(p, stream));
+}

@@ -44,6 +44,26 @@ struct GemmParams {
 hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, hipStream_t stream);
 hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, hipStream_t stream);
 
+// FP8 dispatch permutation: q_dst row r = q_src row index[r] (rows whose
+// index lies outside [0, src_rows) are skipped), scales likewise.  vec: both
+// code pointers and pitches are 16-byte aligned.
+struct DispatchParams {
+    const uint8_t* q_src;
+    int64_t ldq_src;
+    const float* s_src;
+    int64_t lds_src;
+    int64_t src_rows;
+    const int32_t* index;
+    int64_t rows, cols;
+    uint8_t* q_dst;
+    int64_t ldq_dst;
+    float* s_dst;
+    int64_t lds_dst;
+    bool vec;
+};
+
+hipError_t launch_dispatch_rows(const DispatchParams& p, hipStream_t stream);
+
 // Largest group count the grouped GEMM's on-chip tile table holds.
 constexpr int64_t kMaxGroups = 4096;
 

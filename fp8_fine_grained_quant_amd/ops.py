@@ -44,6 +44,8 @@ def _load_library():
     lib.fp8_grouped_gemm.restype = I
     lib.fp8_grouped_gemm.argtypes = [P, I64, P, I64, P, I64, P, P, I64, I64, P, I, I64, I64,
                                      I64, P]
+    lib.fp8_dispatch_rows.restype = I
+    lib.fp8_dispatch_rows.argtypes = [P, I64, P, I64, I64, P, I64, I64, P, I64, P, I64, P]
     lib.fp8q_status_string.restype = ctypes.c_char_p
     lib.fp8q_status_string.argtypes = [I]
     return lib
@@ -230,3 +232,35 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: tor
                                _out_code(c.dtype), c.stride(0), N, K, _stream(a))
     _check(st, "fp8_grouped_gemm")
     return c
+
+
+# --- FP8 dispatch --------------------------------------------------------------
+
+def fp8_dispatch_rows(q_src: torch.Tensor, s_src: torch.Tensor, index: torch.Tensor,
+                      q: torch.Tensor | None = None, s: torch.Tensor | None = None):
+    """Gather token rows of 1x128-quantized activations into expert order.
+
+    q_src [T, C] uint8 codes and s_src [ceil(C/128), T] FP32 scales (the
+    output of fp8_quant_1x128); index int32 [R] on the device, row r taking
+    token index[r] (entries outside [0, T) are skipped).  Returns q [R, C]
+    and s [ceil(C/128), R]."""
+    _require_cuda(q_src, s_src, index)
+    if q_src.dim() != 2 or q_src.stride(1) != 1 or q_src.dtype != torch.uint8:
+        raise ValueError("q_src must be a 2-D uint8 tensor, contiguous along dim 1")
+    T, C = q_src.shape
+    G = (C + 127) // 128
+    if s_src.dim() != 2 or s_src.shape[0] != G or s_src.shape[1] != T or s_src.stride(1) != 1:
+        raise ValueError("s_src must be [ceil(C/128), T], contiguous along dim 1")
+    if index.dtype != torch.int32 or index.dim() != 1 or not index.is_contiguous():
+        raise ValueError("index must be a contiguous int32 vector")
+    R = index.numel()
+    if q is None:
+        q = torch.empty((R, C), dtype=torch.uint8, device=q_src.device)
+    if s is None:
+        s = torch.empty((G, R), dtype=torch.float32, device=q_src.device)
+    _require_cuda(q, s)
+    st = _lib.fp8_dispatch_rows(_ptr(q_src), q_src.stride(0), _ptr(s_src), s_src.stride(0), T,
+                                _ptr(index), R, C, _ptr(q), q.stride(0), _ptr(s), s.stride(0),
+                                _stream(q_src))
+    _check(st, "fp8_dispatch_rows")
+    return q, s

@@ -172,6 +172,28 @@ int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t lds
                      void* c, int c_dtype, int64_t ldc, int64_t N, int64_t K,
                      hipStream_t stream);
 
+/*
+ * fp8_dispatch_rows -- FP8 dispatch permutation.  The activations of the MoE
+ * up-projection are quantized once per token and dispatched to the experts
+ * in FP8, with their scales (jp-study.kr page, passage on quantizing before
+ * the MoE up-projection and dispatching in FP8).  This call builds the
+ * expert-ordered operand of fp8_grouped_gemm from the token-ordered output
+ * of fp8_quant_1x128.  For r < rows, with t = index[r]:
+ *   q_dst[r*ldq_dst + c] = q_src[t*ldq_src + c]   for c < cols;
+ *   s_dst[g*lds_dst + r] = s_src[g*lds_src + t]   for g < ceil(cols/128).
+ *   index : DEVICE int32[rows].  Entries outside [0, src_rows) are skipped:
+ *           that output row and its scales are left unwritten (no fault).
+ *   ldq_src, ldq_dst >= cols; lds_src >= src_rows; lds_dst >= rows.
+ * The source and destination must not overlap.
+ * Alignment: s_src, s_dst and index 4-byte aligned, else FP8Q_EALIGN.  Rows
+ * move with 16-byte accesses when both code pointers and both pitches are
+ * 16-byte aligned, byte accesses otherwise (slower).
+ */
+int fp8_dispatch_rows(const uint8_t* q_src, int64_t ldq_src, const float* s_src,
+                      int64_t lds_src, int64_t src_rows, const int32_t* index,
+                      int64_t rows, int64_t cols, uint8_t* q_dst, int64_t ldq_dst,
+                      float* s_dst, int64_t lds_dst, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fp8q_status_string(int status);
 

@@ -28,10 +28,10 @@ def declared_functions():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("fp8_quant_1x128", "fp8_quant_128x128", "fp8_blockscaled_gemm", "fp8_grouped_gemm",
-              "fp8q_status_string"):
+              "fp8_dispatch_rows", "fp8q_status_string"):
         assert n in names
 
 
@@ -128,3 +128,19 @@ def test_grouped_gemm_validation(lib):
     assert ggemm(lib, G=100000) == EUNSUPPORTED
     assert ggemm(lib, K=200, lda=208, ldb=208) == EUNSUPPORTED
     assert ggemm(lib, ldsa=100) == EINVAL
+
+
+def disp(lib, qs=A, ldqs=7168, ss=A, lds_s=100, T=100, idx=A, R=300, C=7168, qd=A, ldqd=7168, sd=A,
+         lds_d=300):
+    return lib.fp8_dispatch_rows(qs, ldqs, ss, lds_s, T, idx, R, C, qd, ldqd, sd, lds_d, None)
+
+
+def test_dispatch_rows_validation(lib):
+    assert disp(lib, R=-1) == EINVAL and disp(lib, C=-1) == EINVAL and disp(lib, T=-1) == EINVAL
+    assert disp(lib, R=0) == OK and disp(lib, C=0) == OK              # no-ops
+    for k in ("qs", "ss", "idx", "qd", "sd"):
+        assert disp(lib, **{k: None}) == EINVAL
+    assert disp(lib, ldqs=7000) == EINVAL and disp(lib, ldqd=7000) == EINVAL
+    assert disp(lib, lds_s=99) == EINVAL and disp(lib, lds_d=299) == EINVAL
+    assert disp(lib, ss=A + 2) == EALIGN and disp(lib, sd=A + 1) == EALIGN
+    assert disp(lib, idx=A + 2) == EALIGN
