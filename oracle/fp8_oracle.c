@@ -39,6 +39,12 @@
  *     products of two E4M3 values is exact in fp64, so the only roundings
  *     are the scale product times partial and the running sum over blocks.
  *
+ * A second scale rule serves the hardware-scaled variant: the scale is the
+ * power of two 2^e (smallest e with amax <= 448 * 2^e, e in [-127, 127]),
+ * the value an E8M0 exponent carries, so that the matrix instruction can
+ * apply it.  The pages ask for hardware that applies group scales inside
+ * the matrix multiply (why-be.why-be.co.kr page, hardware-design passage).
+ *
  * Parity pins: every function here is checked by the CPU test-suite against
  * closed forms, a brute-force nearest-value encoder, PyTorch's own E4M3 cast,
  * exact rational arithmetic and integer matmul (tests/test_oracle_*.py).
@@ -141,6 +147,31 @@ OR_EXPORT void or_group_scale(float amax, float* s, float* inv) {
     *inv = iv;
 }
 
+/* Power-of-two scale rule (the scale an E8M0 exponent can carry): s = 2^e
+ * with e the smallest integer such that amax <= 448 * 2^e, clamped to the
+ * E8M0 range [-127, 127] (amax == 0 gives e = -127); inv = 2^-e.  Found by
+ * direct search in fp64, where 448 * 2^e and amax are exact. */
+OR_EXPORT void or_group_scale_pow2(float amax, float* s, float* inv) {
+    int e = -127;
+    if (amax > 0.0f) {
+        double a = (double)amax;
+        e = 0;
+        while (ldexp(448.0, e) < a) ++e;
+        while (ldexp(448.0, e - 1) >= a) --e;
+        if (e < -127) e = -127;
+        if (e > 127) e = 127;
+    }
+    *s = ldexpf(1.0f, e);
+    *inv = ldexpf(1.0f, -e);
+}
+
+enum { OR_RULE_FP32 = 0, OR_RULE_POW2 = 1 };
+
+static void group_scale_rule(int rule, float amax, float* s, float* inv) {
+    if (rule == OR_RULE_POW2) or_group_scale_pow2(amax, s, inv);
+    else or_group_scale(amax, s, inv);
+}
+
 static uint8_t quant_one(float x, float inv) {
     volatile float p = x * inv;         /* one FP32 product, RNE */
     return or_e4m3_encode(p);
@@ -154,6 +185,7 @@ typedef struct {
     const void* x; int dtype; int64_t rows, cols, xs_r, xs_c;
     uint8_t* q; int64_t ldq; float* s; int64_t lds;
     int64_t r0, r1;
+    int rule;
 } q1x128_job;
 
 static void* q1x128_worker(void* p) {
@@ -168,7 +200,7 @@ static void* q1x128_worker(void* p) {
                 if (v > amax) amax = v;
             }
             float s, inv;
-            or_group_scale(amax, &s, &inv);
+            group_scale_rule(j->rule, amax, &s, &inv);
             j->s[g * j->lds + r] = s;
             for (int64_t c = c0; c < c1; ++c)
                 j->q[r * j->ldq + c] =
@@ -185,20 +217,27 @@ static int clamp_threads(int nthreads, int64_t work) {
     return nthreads;
 }
 
-OR_EXPORT void or_quant_1x128(const void* x, int dtype, int64_t rows, int64_t cols,
-                              int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq,
-                              float* s, int64_t lds, int nthreads) {
+OR_EXPORT void or_quant_1x128_rule(const void* x, int dtype, int64_t rows, int64_t cols,
+                                   int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq,
+                                   float* s, int64_t lds, int nthreads, int rule) {
     ensure_tables();
     nthreads = clamp_threads(nthreads, rows);
     pthread_t th[256];
     q1x128_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         q1x128_job j = {x, dtype, rows, cols, xs_r, xs_c, q, ldq, s, lds,
-                        rows * t / nthreads, rows * (t + 1) / nthreads};
+                        rows * t / nthreads, rows * (t + 1) / nthreads, rule};
         jobs[t] = j;
         pthread_create(&th[t], NULL, q1x128_worker, &jobs[t]);
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+OR_EXPORT void or_quant_1x128(const void* x, int dtype, int64_t rows, int64_t cols,
+                              int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq,
+                              float* s, int64_t lds, int nthreads) {
+    or_quant_1x128_rule(x, dtype, rows, cols, xs_r, xs_c, q, ldq, s, lds, nthreads,
+                        OR_RULE_FP32);
 }
 
 /* 128x128 blocks of a row-major [rows, cols] matrix with leading dimension
@@ -208,6 +247,7 @@ typedef struct {
     const void* w; int dtype; int64_t rows, cols, ldw;
     uint8_t* q; int64_t ldq; float* s; uint8_t* q_t; int64_t ldqt;
     int64_t b0, b1; /* block-row range */
+    int rule;
 } q128_job;
 
 static void* q128_worker(void* p) {
@@ -224,7 +264,7 @@ static void* q128_worker(void* p) {
                     if (v > amax) amax = v;
                 }
             float s, inv;
-            or_group_scale(amax, &s, &inv);
+            group_scale_rule(j->rule, amax, &s, &inv);
             j->s[bi * gc + bj] = s;
             for (int64_t r = r0; r < r1; ++r)
                 for (int64_t c = c0; c < c1; ++c) {
@@ -237,9 +277,9 @@ static void* q128_worker(void* p) {
     return NULL;
 }
 
-OR_EXPORT void or_quant_128x128(const void* w, int dtype, int64_t rows, int64_t cols,
-                                int64_t ldw, uint8_t* q, int64_t ldq, float* s,
-                                uint8_t* q_t, int64_t ldqt, int nthreads) {
+OR_EXPORT void or_quant_128x128_rule(const void* w, int dtype, int64_t rows, int64_t cols,
+                                     int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                     uint8_t* q_t, int64_t ldqt, int nthreads, int rule) {
     ensure_tables();
     int64_t gr = (rows + 127) / 128;
     nthreads = clamp_threads(nthreads, gr);
@@ -247,11 +287,18 @@ OR_EXPORT void or_quant_128x128(const void* w, int dtype, int64_t rows, int64_t 
     q128_job jobs[256];
     for (int t = 0; t < nthreads; ++t) {
         q128_job j = {w, dtype, rows, cols, ldw, q, ldq, s, q_t, ldqt,
-                      gr * t / nthreads, gr * (t + 1) / nthreads};
+                      gr * t / nthreads, gr * (t + 1) / nthreads, rule};
         jobs[t] = j;
         pthread_create(&th[t], NULL, q128_worker, &jobs[t]);
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+OR_EXPORT void or_quant_128x128(const void* w, int dtype, int64_t rows, int64_t cols,
+                                int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                                uint8_t* q_t, int64_t ldqt, int nthreads) {
+    or_quant_128x128_rule(w, dtype, rows, cols, ldw, q, ldq, s, q_t, ldqt, nthreads,
+                          OR_RULE_FP32);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -57,8 +57,11 @@ def _load():
     lib.or_e4m3_encode_array.argtypes = [P, P, I64]
     lib.or_e4m3_decode_array.argtypes = [P, P, I64]
     lib.or_group_scale.argtypes = [ctypes.c_float, P, P]
+    lib.or_group_scale_pow2.argtypes = [ctypes.c_float, P, P]
     lib.or_quant_1x128.argtypes = [P, I, I64, I64, I64, I64, P, I64, P, I64, I]
     lib.or_quant_128x128.argtypes = [P, I, I64, I64, I64, P, I64, P, P, I64, I]
+    lib.or_quant_1x128_rule.argtypes = [P, I, I64, I64, I64, I64, P, I64, P, I64, I, I]
+    lib.or_quant_128x128_rule.argtypes = [P, I, I64, I64, I64, P, I64, P, P, I64, I, I]
     lib.or_gemm_exact.argtypes = [P, I64, P, I64, P, I64, P, I, I64, I64, I64, I64, I64,
                                   P, P, I]
     lib.or_gemm_exact_elems.argtypes = [P, I64, P, I64, P, I64, P, I, I64, I64, I64,
@@ -109,9 +112,23 @@ def group_scale(amax: float):
     return np.float32(s.value), np.float32(inv.value)
 
 
+# scale rules: FP32 amax/448 (the method's), or the power of two an E8M0
+# exponent carries (smallest 2^e with amax <= 448 * 2^e, e in [-127, 127])
+RULE_FP32, RULE_POW2 = 0, 1
+
+
+def group_scale_pow2(amax: float):
+    """(s, inv) = (2^e, 2^-e) for one group under the power-of-two rule."""
+    s = ctypes.c_float()
+    inv = ctypes.c_float()
+    _load().or_group_scale_pow2(ctypes.c_float(amax), ctypes.byref(s), ctypes.byref(inv))
+    return np.float32(s.value), np.float32(inv.value)
+
+
 # --- quantization -----------------------------------------------------------
 
-def quant_1x128(x: np.ndarray, transposed: bool = False, threads: int | None = None):
+def quant_1x128(x: np.ndarray, transposed: bool = False, threads: int | None = None,
+                rule: int = RULE_FP32):
     """1x128 groups along the last axis of the 2-D array ``x``.
 
     With ``transposed=True`` the groups run along the FIRST axis instead
@@ -129,12 +146,13 @@ def quant_1x128(x: np.ndarray, transposed: bool = False, threads: int | None = N
     g = (cols + 127) // 128
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty((g, rows), dtype=np.float32)
-    _load().or_quant_1x128(_ptr(x), dt, rows, cols, xs_r, xs_c, _ptr(q), cols, _ptr(s),
-                           rows, threads or host_threads())
+    _load().or_quant_1x128_rule(_ptr(x), dt, rows, cols, xs_r, xs_c, _ptr(q), cols, _ptr(s),
+                                rows, threads or host_threads(), rule)
     return q, s
 
 
-def quant_128x128(w: np.ndarray, with_transpose: bool = False, threads: int | None = None):
+def quant_128x128(w: np.ndarray, with_transpose: bool = False, threads: int | None = None,
+                  rule: int = RULE_FP32):
     """128x128 blocks.  Returns (q, s, q_t) with s[i, j] the scale of block
     (i, j) and q_t the transposed codes (or None)."""
     w = np.ascontiguousarray(w)
@@ -143,8 +161,8 @@ def quant_128x128(w: np.ndarray, with_transpose: bool = False, threads: int | No
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty(((rows + 127) // 128, (cols + 127) // 128), dtype=np.float32)
     q_t = np.empty((cols, rows), dtype=np.uint8) if with_transpose else None
-    _load().or_quant_128x128(_ptr(w), dt, rows, cols, cols, _ptr(q), cols, _ptr(s),
-                             _ptr(q_t), rows, threads or host_threads())
+    _load().or_quant_128x128_rule(_ptr(w), dt, rows, cols, cols, _ptr(q), cols, _ptr(s),
+                                  _ptr(q_t), rows, threads or host_threads(), rule)
     return q, s, q_t
 
 
