@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace fp8q {
 
 // Largest finite OCP E4M3 magnitude: 1.75 * 2^8.
@@ -38,6 +40,29 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 __device__ __forceinline__ void group_scale(float amax, float& s, float& inv) {
     s = amax / kE4M3Max;
     inv = fminf(kE4M3Max / amax, kFltMax);
+}
+
+// Power-of-two rule (the value an E8M0 exponent carries): s = 2^e with e the
+// smallest integer such that amax <= 448 * 2^e, clamped to [-127, 127], and
+// inv = 2^-e.  For a normal amax = 1.f * 2^k, 448 * 2^e = 1.75 * 2^(8+e), so
+// e = k - 8 when 1.f <= 1.75 (mantissa field <= 0x600000) and k - 7 above;
+// zero and subnormal amax (k <= -127) clamp to e = -127.  s = 2^-127 is the
+// FP32 subnormal 0x00400000; inv's exponent field 127 - e stays in [6, 254].
+__device__ __forceinline__ void group_scale_pow2(float amax, float& s, float& inv) {
+    const uint32_t b = __float_as_uint(amax);
+    int e = -127;
+    if (b >= 0x00800000u) {
+        const int k = (int)(b >> 23) - 127;
+        e = max(k - 8 + ((b & 0x7FFFFFu) > 0x600000u ? 1 : 0), -127);
+    }
+    s = e >= -126 ? __uint_as_float((uint32_t)(e + 127) << 23) : __uint_as_float(0x00400000u);
+    inv = __uint_as_float((uint32_t)(127 - e) << 23);
+}
+
+template <int RULE>
+__device__ __forceinline__ void group_scale_rule(float amax, float& s, float& inv) {
+    if (RULE == kRulePow2) group_scale_pow2(amax, s, inv);
+    else group_scale(amax, s, inv);
 }
 
 // Encode 4 FP32 values (already multiplied by inv) into one dword, byte i =

@@ -27,9 +27,11 @@ FP8Q_API const char* fp8q_status_string(int status) {
     }
 }
 
-FP8Q_API int fp8_quant_1x128(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t xs_r,
-                             int64_t xs_c, uint8_t* q, int64_t ldq, float* s, int64_t lds,
-                             hipStream_t stream) {
+namespace {
+
+int quant_1x128_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t xs_r,
+                     int64_t xs_c, uint8_t* q, int64_t ldq, float* s, int64_t lds, int rule,
+                     hipStream_t stream) {
     if (rows < 0 || cols < 0) return FP8Q_EINVAL;
     if (x_dtype != FP8Q_F32 && x_dtype != FP8Q_BF16) return FP8Q_EINVAL;
     if (rows == 0 || cols == 0) return FP8Q_OK;
@@ -42,21 +44,22 @@ FP8Q_API int fp8_quant_1x128(const void* x, int x_dtype, int64_t rows, int64_t c
         // row-contiguous input
         const int64_t ldx = rows == 1 ? cols : xs_r;
         return launch_status(fp8q::launch_quant_rows(x, x_dtype, rows, cols, ldx, q, ldq, s,
-                                                     lds, stream));
+                                                     lds, rule, stream));
     }
     if (xs_r == 1 && (xs_c >= rows || cols == 1)) {
         // Stored transposed: physical tensor [cols, rows] with row pitch xs_c;
         // 128x1 groups along its rows, codes written transposed.
         const int64_t ldx = cols == 1 ? rows : xs_c;
         return launch_status(fp8q::launch_quant_tiles(x, x_dtype, fp8q::kTileCols, cols, rows,
-                                                      ldx, nullptr, 0, q, ldq, s, lds, stream));
+                                                      ldx, nullptr, 0, q, ldq, s, lds, rule,
+                                                      stream));
     }
     return FP8Q_EINVAL;
 }
 
-FP8Q_API int fp8_quant_128x128(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
-                               uint8_t* q, int64_t ldq, float* s, uint8_t* q_t, int64_t ldqt,
-                               hipStream_t stream) {
+int quant_128x128_impl(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                       uint8_t* q, int64_t ldq, float* s, uint8_t* q_t, int64_t ldqt, int rule,
+                       hipStream_t stream) {
     if (rows < 0 || cols < 0) return FP8Q_EINVAL;
     if (w_dtype != FP8Q_F32 && w_dtype != FP8Q_BF16) return FP8Q_EINVAL;
     if (rows == 0 || cols == 0) return FP8Q_OK;
@@ -65,7 +68,37 @@ FP8Q_API int fp8_quant_128x128(const void* w, int w_dtype, int64_t rows, int64_t
     if (q_t && ldqt < rows) return FP8Q_EINVAL;
     if (!aligned(w, w_dtype == FP8Q_BF16 ? 2 : 4) || !aligned(s, 4)) return FP8Q_EALIGN;
     return launch_status(fp8q::launch_quant_tiles(w, w_dtype, fp8q::kTileBlock, rows, cols, ldw, q,
-                                                  ldq, q_t, ldqt, s, 0, stream));
+                                                  ldq, q_t, ldqt, s, 0, rule, stream));
+}
+
+}  // namespace
+
+FP8Q_API int fp8_quant_1x128(const void* x, int x_dtype, int64_t rows, int64_t cols, int64_t xs_r,
+                             int64_t xs_c, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                             hipStream_t stream) {
+    return quant_1x128_impl(x, x_dtype, rows, cols, xs_r, xs_c, q, ldq, s, lds, fp8q::kRuleFP32,
+                            stream);
+}
+
+FP8Q_API int fp8_quant_1x128_pow2(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                                  int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq, float* s,
+                                  int64_t lds, hipStream_t stream) {
+    return quant_1x128_impl(x, x_dtype, rows, cols, xs_r, xs_c, q, ldq, s, lds, fp8q::kRulePow2,
+                            stream);
+}
+
+FP8Q_API int fp8_quant_128x128(const void* w, int w_dtype, int64_t rows, int64_t cols, int64_t ldw,
+                               uint8_t* q, int64_t ldq, float* s, uint8_t* q_t, int64_t ldqt,
+                               hipStream_t stream) {
+    return quant_128x128_impl(w, w_dtype, rows, cols, ldw, q, ldq, s, q_t, ldqt, fp8q::kRuleFP32,
+                              stream);
+}
+
+FP8Q_API int fp8_quant_128x128_pow2(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                                    int64_t ldw, uint8_t* q, int64_t ldq, float* s, uint8_t* q_t,
+                                    int64_t ldqt, hipStream_t stream) {
+    return quant_128x128_impl(w, w_dtype, rows, cols, ldw, q, ldq, s, q_t, ldqt, fp8q::kRulePow2,
+                              stream);
 }
 
 namespace {
@@ -89,11 +122,12 @@ int check_gemm_common(const uint8_t* a, int64_t lda, const float* sa, int64_t ld
 
 }  // namespace
 
-FP8Q_API int fp8_blockscaled_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
-                                  const uint8_t* b, int64_t ldb, const float* sb,
-                                  int b_scale_mode, int64_t sbs0, int64_t sbs1, void* c,
-                                  int c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                                  hipStream_t stream) {
+namespace {
+
+int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, const uint8_t* b,
+              int64_t ldb, const float* sb, int b_scale_mode, int64_t sbs0, int64_t sbs1, void* c,
+              int c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K, bool pow2,
+              hipStream_t stream) {
     if (M == 0 || N == 0) {
         if (M < 0 || N < 0) return FP8Q_EINVAL;
         return FP8Q_OK;
@@ -112,14 +146,13 @@ FP8Q_API int fp8_blockscaled_gemm(const uint8_t* a, int64_t lda, const float* sa
     p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;
     p.b = b; p.ldb = ldb; p.sb = sb; p.sbs0 = sbs0; p.sbs1 = sbs1;
     p.c = c; p.ldc = ldc; p.M = M; p.N = N; p.K = K;
-    return launch_status(fp8q::launch_gemm(p, b_scale_mode, c_dtype, stream));
+    return launch_status(fp8q::launch_gemm(p, b_scale_mode, c_dtype, pow2, stream));
 }
 
-FP8Q_API int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
-                              const uint8_t* b, int64_t ldb, const float* sb,
-                              const int32_t* offsets, int64_t num_groups, int64_t M_total,
-                              void* c, int c_dtype, int64_t ldc, int64_t N, int64_t K,
-                              hipStream_t stream) {
+int grouped_gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                      const uint8_t* b, int64_t ldb, const float* sb, const int32_t* offsets,
+                      int64_t num_groups, int64_t M_total, void* c, int c_dtype, int64_t ldc,
+                      int64_t N, int64_t K, bool pow2, hipStream_t stream) {
     if (num_groups <= 0 || M_total < 0 || N < 0) return FP8Q_EINVAL;
     if (M_total == 0 || N == 0) return FP8Q_OK;
     if (!offsets) return FP8Q_EINVAL;
@@ -135,7 +168,45 @@ FP8Q_API int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, in
     p.b = b; p.ldb = ldb; p.sb = sb; p.sbs0 = K / 128; p.sbs1 = 1;
     p.c = c; p.ldc = ldc; p.M = M_total; p.N = N; p.K = K;
     p.offsets = offsets; p.num_groups = num_groups;
-    return launch_status(fp8q::launch_grouped_gemm(p, c_dtype, stream));
+    return launch_status(fp8q::launch_grouped_gemm(p, c_dtype, pow2, stream));
+}
+
+}  // namespace
+
+FP8Q_API int fp8_blockscaled_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                  const uint8_t* b, int64_t ldb, const float* sb,
+                                  int b_scale_mode, int64_t sbs0, int64_t sbs1, void* c,
+                                  int c_dtype, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                  hipStream_t stream) {
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, b_scale_mode, sbs0, sbs1, c, c_dtype, ldc, M, N,
+                     K, false, stream);
+}
+
+FP8Q_API int fp8_blockscaled_gemm_pow2(const uint8_t* a, int64_t lda, const float* sa,
+                                       int64_t ldsa, const uint8_t* b, int64_t ldb,
+                                       const float* sb, int b_scale_mode, int64_t sbs0,
+                                       int64_t sbs1, void* c, int c_dtype, int64_t ldc, int64_t M,
+                                       int64_t N, int64_t K, hipStream_t stream) {
+    return gemm_impl(a, lda, sa, ldsa, b, ldb, sb, b_scale_mode, sbs0, sbs1, c, c_dtype, ldc, M, N,
+                     K, true, stream);
+}
+
+FP8Q_API int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                              const uint8_t* b, int64_t ldb, const float* sb,
+                              const int32_t* offsets, int64_t num_groups, int64_t M_total,
+                              void* c, int c_dtype, int64_t ldc, int64_t N, int64_t K,
+                              hipStream_t stream) {
+    return grouped_gemm_impl(a, lda, sa, ldsa, b, ldb, sb, offsets, num_groups, M_total, c,
+                             c_dtype, ldc, N, K, false, stream);
+}
+
+FP8Q_API int fp8_grouped_gemm_pow2(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                                   const uint8_t* b, int64_t ldb, const float* sb,
+                                   const int32_t* offsets, int64_t num_groups, int64_t M_total,
+                                   void* c, int c_dtype, int64_t ldc, int64_t N, int64_t K,
+                                   hipStream_t stream) {
+    return grouped_gemm_impl(a, lda, sa, ldsa, b, ldb, sb, offsets, num_groups, M_total, c,
+                             c_dtype, ldc, N, K, true, stream);
 }
 
 FP8Q_API int fp8_dispatch_rows(const uint8_t* q_src, int64_t ldq_src, const float* s_src,

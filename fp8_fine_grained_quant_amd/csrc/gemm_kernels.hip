@@ -116,6 +116,21 @@ __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b) {
         a, b, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kOneE8M0, 0, kOneE8M0);
 }
 
+// Power-of-two scales applied by the instruction itself: lane l's scale
+// operands are the E8M0 exponents of its operand-A row (l & 15) and
+// operand-B row (l & 15), used for every 32-wide K group of the lane's
+// fragment; the product accumulates onto c.
+__device__ __forceinline__ v4f mfma_f8_scaled(const v8i& a, const v8i& b, const v4f& c,
+                                              uint32_t scale_a, uint32_t scale_b) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)scale_a, 0,
+                                                            (int)scale_b);
+}
+
+// E8M0 exponent of an FP32 power of two 2^e, e in [-127, 127]: its biased
+// exponent field (2^-127, an FP32 subnormal, gives 0).  Mantissa bits are
+// ignored.
+__device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
+
 // Everything a wave needs to stream one K step of A, B and the scales into
 // an LDS stage.
 struct LoadCtx {
@@ -165,7 +180,7 @@ __device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const 
     }
 }
 
-template <int SCALE_MODE, int OUT, bool GROUPED>
+template <int SCALE_MODE, int OUT, bool GROUPED, bool POW2>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
     // [stage][0..255]: sa of the tile's rows; [stage][256..511]: ROW128: sb
@@ -315,6 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     v8i af[4], bf[3];
     float sc[4];
+    uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of sa rows, of the block's sb
     auto load_step_frags = [&](int st) {
         const uint8_t* sa_ = stage_a(st);
         const uint8_t* sb_ = stage_b(st);
@@ -323,9 +339,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
         bf[1] = frag32(sb_, wn * 8 + 1, lane);
         bf[2] = frag32(sb_, wn * 8 + 2, lane);
-        const float sbv = SCALE_MODE == kScaleBlock128 ? smem_s[st][BM + wn] : 1.0f;
+        if constexpr (POW2) {
+            if (SCALE_MODE == kScaleBlock128) sbb = e8m0_of(smem_s[st][BM + wn]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[i] = smem_s[st][wm * kWaveM + i * 16 + r16] * sbv;
+            for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[st][wm * kWaveM + i * 16 + r16]);
+        } else {
+            const float sbv = SCALE_MODE == kScaleBlock128 ? smem_s[st][BM + wn] : 1.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sc[i] = smem_s[st][wm * kWaveM + i * 16 + r16] * sbv;
+        }
     };
 
     copy_step(0, 0);
@@ -337,8 +359,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const int cur = kb & 1;
         const uint8_t* cb_ = stage_b(cur);
         v4f part[2][4];
+        // POW2, ROW128: the E8M0 exponent of the B row (l & 15) of column block j
+        auto sb_e8m0 = [&](int j) -> uint32_t {
+            if (SCALE_MODE == kScaleBlock128) return sbb;
+            return e8m0_of(smem_s[cur][BM + wn * kWaveN + j * 16 + r16]);
+        };
+        if constexpr (POW2) {
+            const uint32_t s0 = sb_e8m0(0);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[0][i] = mfma_f8(bf[0], af[i]);
+            for (int i = 0; i < 4; ++i) acc[i][0] = mfma_f8_scaled(bf[0], af[i], acc[i][0], s0, sab[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[0][i] = mfma_f8(bf[0], af[i]);
+        }
         // ROW128: the four column scales of block j for this lane
         auto row_scales = [&](int j) {
             if (SCALE_MODE != kScaleRow128) return make_float4(1.f, 1.f, 1.f, 1.f);
@@ -348,11 +381,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int j = 1; j <= 6; ++j) {
             if (j + 2 <= 7) bf[(j + 2) % 3] = frag32(cb_, wn * 8 + j + 2, lane);
+            if constexpr (POW2) {
+                const uint32_t sj = sb_e8m0(j);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) part[j & 1][i] = mfma_f8(bf[j % 3], af[i]);
-            const float4 sbq = row_scales(j - 1);
+                for (int i = 0; i < 4; ++i)
+                    acc[i][j] = mfma_f8_scaled(bf[j % 3], af[i], acc[i][j], sj, sab[i]);
+            } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][j - 1], part[(j - 1) & 1][i], sc[i], sbq);
+                for (int i = 0; i < 4; ++i) part[j & 1][i] = mfma_f8(bf[j % 3], af[i]);
+                const float4 sbq = row_scales(j - 1);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    promote<SCALE_MODE>(acc[i][j - 1], part[(j - 1) & 1][i], sc[i], sbq);
+            }
             // issue order inside the block: MFMA, 4 promotion FMAs, with the
             // two fragment reads of block j+2 slotted after the first two
             // MFMAs -- the other wave of the SIMD fills the MFMA shadow
@@ -367,23 +408,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
         }
         const float4 sbq6 = row_scales(6), sbq7 = row_scales(7);
+        const uint32_t s7 = POW2 ? sb_e8m0(7) : 0u;
         // every LDS read of stage cur has been issued: release it, and make
         // step kb+1 (copied into cur^1 during the previous step) visible
         stage_barrier();
         __builtin_amdgcn_sched_barrier(0);
         v4f last[4];
+        if constexpr (POW2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) last[i] = mfma_f8(bf[7 % 3], af[i]);
+            for (int i = 0; i < 4; ++i) acc[i][7] = mfma_f8_scaled(bf[7 % 3], af[i], acc[i][7], s7, sab[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) last[i] = mfma_f8(bf[7 % 3], af[i]);
+        }
         float sc_old[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) sc_old[i] = sc[i];
         copy_step(kb + 2, cur);
         __builtin_amdgcn_sched_barrier(0);
         load_step_frags(cur ^ 1);   // after the last step: unused, harmless reads
+        if constexpr (!POW2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][6], part[0][i], sc_old[i], sbq6);
+            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][6], part[0][i], sc_old[i], sbq6);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][7], last[i], sc_old[i], sbq7);
+            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][7], last[i], sc_old[i], sbq7);
+        }
     }
     wait_vm_all();
 
@@ -419,29 +468,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     }
 }
 
-hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, hipStream_t stream) {
+hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool pow2,
+                       hipStream_t stream) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
-#define FP8Q_GEMM(SM, OD) hipLaunchKernelGGL((gemm_kernel<SM, OD, false>), grid, block, 0, stream, p)
+#define FP8Q_GEMM(SM, OD, P2) \
+    hipLaunchKernelGGL((gemm_kernel<SM, OD, false, P2>), grid, block, 0, stream, p)
+#define FP8Q_GEMM_P2(SM, OD)                  \
+    do {                                      \
+        if (pow2) FP8Q_GEMM(SM, OD, true);    \
+        else FP8Q_GEMM(SM, OD, false);        \
+    } while (0)
     if (scale_mode == kScaleBlock128) {
-        if (out_dtype == kBF16) FP8Q_GEMM(kScaleBlock128, kBF16);
-        else FP8Q_GEMM(kScaleBlock128, kF32);
+        if (out_dtype == kBF16) FP8Q_GEMM_P2(kScaleBlock128, kBF16);
+        else FP8Q_GEMM_P2(kScaleBlock128, kF32);
     } else {
-        if (out_dtype == kBF16) FP8Q_GEMM(kScaleRow128, kBF16);
-        else FP8Q_GEMM(kScaleRow128, kF32);
+        if (out_dtype == kBF16) FP8Q_GEMM_P2(kScaleRow128, kBF16);
+        else FP8Q_GEMM_P2(kScaleRow128, kF32);
     }
+#undef FP8Q_GEMM_P2
 #undef FP8Q_GEMM
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, hipStream_t stream) {
+hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, bool pow2, hipStream_t stream) {
     // upper bound on the tile count: sum_g ceil(rows_g/BM) <= M/BM + groups
     const int64_t tiles = ((p.M + BM - 1) / BM + p.num_groups) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
-    if (out_dtype == kBF16)
-        hipLaunchKernelGGL((gemm_kernel<kScaleBlock128, kBF16, true>), grid, block, 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_kernel<kScaleBlock128, kF32, true>), grid, block, 0, stream, p);
+#define FP8Q_GGEMM(OD, P2) \
+    hipLaunchKernelGGL((gemm_kernel<kScaleBlock128, OD, true, P2>), grid, block, 0, stream, p)
+    if (out_dtype == kBF16) {
+        if (pow2) FP8Q_GGEMM(kBF16, true);
+        else FP8Q_GGEMM(kBF16, false);
+    } else {
+        if (pow2) FP8Q_GGEMM(kF32, true);
+        else FP8Q_GGEMM(kF32, false);
+    }
+#undef FP8Q_GGEMM
     return hipGetLastError();
 }
 

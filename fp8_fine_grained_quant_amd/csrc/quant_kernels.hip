@@ -117,7 +117,7 @@ __device__ __forceinline__ void store8(uint8_t* row, int64_t c0, int64_t cols, u
 }
 
 // One group: 16 lanes x 8 elements.  Every lane of the DPP row takes part.
-template <int DT>
+template <int DT, int RULE>
 __device__ __forceinline__ void quant_group_1x128(const float v[8], uint8_t* qrow, int64_t c0,
                                                   int64_t cols, float* s_out, bool lead,
                                                   bool vout) {
@@ -126,7 +126,7 @@ __device__ __forceinline__ void quant_group_1x128(const float v[8], uint8_t* qro
     for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(fabsf(v[i])));
     m = row16_max_u32(m);
     float s, inv;
-    group_scale(__uint_as_float(m), s, inv);
+    group_scale_rule<RULE>(__uint_as_float(m), s, inv);
     uint32_t lo = enc4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
     uint32_t hi = enc4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     store8(qrow, c0, cols, lo, hi, vout);
@@ -136,7 +136,7 @@ __device__ __forceinline__ void quant_group_1x128(const float v[8], uint8_t* qro
 // Grid: blocks of 4 waves; wave w of block b handles rows b*4+w (grid-strided);
 // within a row, the 4 DPP rows (slices) of the wave take groups g = slice,
 // slice+4, ... so one wave-load covers 4 consecutive groups (1 KB of BF16).
-template <int DT>
+template <int DT, int RULE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ldx,
                                                          uint8_t* __restrict__ q, int64_t ldq,
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
             for (int u = 0; u < kRowUnroll; ++u) {
                 const int64_t g = g0 + 4 * u + slice;
                 if (g < groups)
-                    quant_group_1x128<DT>(v[u], qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0,
+                    quant_group_1x128<DT, RULE>(v[u], qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0,
                                           vout);
             }
         }
@@ -200,7 +200,7 @@ __device__ __forceinline__ uint32_t code_byte(uint32_t lo, uint32_t hi, int j) {
     return ((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4)))) & 0xFFu;
 }
 
-template <int DT, int MODE>
+template <int DT, int MODE, int RULE>
 __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ldx,
                                                          uint8_t* __restrict__ q, int64_t ldq,
@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
         __syncthreads();
         m = max(max(red[0], red[1]), max(red[2], red[3]));
         float sc, iv;
-        group_scale(__uint_as_float(m), sc, iv);
+        group_scale_rule<RULE>(__uint_as_float(m), sc, iv);
         if (tid == 0) s[ti * tiles_c + tj] = sc;
 #pragma unroll
         for (int j = 0; j < 8; ++j) inv[j] = iv;
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
             const int c = 8 * b + j;
             uint32_t mm = max(max(red[c], red[128 + c]), max(red[256 + c], red[384 + c]));
             float sc, iv;
-            group_scale(__uint_as_float(mm), sc, iv);
+            group_scale_rule<RULE>(__uint_as_float(mm), sc, iv);
             inv[j] = iv;
             // logical output row = input column; scale index [tile row][column]
             if (a == 0 && c0 + j < cols) s[ti * lds + c0 + j] = sc;
@@ -305,41 +305,53 @@ static bool is_aligned(const void* p, uintptr_t a) {
 }
 
 hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
-                             uint8_t* q, int64_t ldq, float* s, int64_t lds, hipStream_t stream) {
+                             uint8_t* q, int64_t ldq, float* s, int64_t lds, int rule,
+                             hipStream_t stream) {
     int64_t blocks = (rows + 3) / 4;
     if (blocks > 65536 * 8) blocks = 65536 * 8;
     dim3 grid((unsigned)blocks), block(256);
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vout = is_aligned(q, 8) && ldq % 8 == 0;
-    if (dtype == kBF16)
-        hipLaunchKernelGGL(quant_rows_kernel<kBF16>, grid, block, 0, stream, x, rows, cols, ldx, q,
-                           ldq, s, lds, vin, vout);
-    else
-        hipLaunchKernelGGL(quant_rows_kernel<kF32>, grid, block, 0, stream, x, rows, cols, ldx, q,
-                           ldq, s, lds, vin, vout);
+#define FP8Q_LAUNCH_ROWS(DT, RL)                                                               \
+    hipLaunchKernelGGL((quant_rows_kernel<DT, RL>), grid, block, 0, stream, x, rows, cols, ldx, q, \
+                       ldq, s, lds, vin, vout)
+    if (dtype == kBF16) {
+        if (rule == kRulePow2) FP8Q_LAUNCH_ROWS(kBF16, kRulePow2);
+        else FP8Q_LAUNCH_ROWS(kBF16, kRuleFP32);
+    } else {
+        if (rule == kRulePow2) FP8Q_LAUNCH_ROWS(kF32, kRulePow2);
+        else FP8Q_LAUNCH_ROWS(kF32, kRuleFP32);
+    }
+#undef FP8Q_LAUNCH_ROWS
     return hipGetLastError();
 }
 
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
-                              float* s, int64_t lds, hipStream_t stream) {
+                              float* s, int64_t lds, int rule, hipStream_t stream) {
     const int64_t tr = (rows + 127) / 128, tc = (cols + 127) / 128;
     dim3 grid((unsigned)(tr * tc)), block(256);
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vq = q != nullptr && is_aligned(q, 8) && ldq % 8 == 0;
     const bool vqt = qt != nullptr && is_aligned(qt, 8) && ldqt % 8 == 0;
-#define FP8Q_LAUNCH_TILE(DT, MD)                                                                 \
-    hipLaunchKernelGGL((quant_tile_kernel<DT, MD>), grid, block, 0, stream, x, rows, cols, ldx, q, \
-                       ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
+#define FP8Q_LAUNCH_TILE(DT, MD, RL)                                                     \
+    hipLaunchKernelGGL((quant_tile_kernel<DT, MD, RL>), grid, block, 0, stream, x, rows, cols, \
+                       ldx, q, ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
+#define FP8Q_LAUNCH_TILE_RULE(DT, MD)                          \
+    do {                                                       \
+        if (rule == kRulePow2) FP8Q_LAUNCH_TILE(DT, MD, kRulePow2); \
+        else FP8Q_LAUNCH_TILE(DT, MD, kRuleFP32);              \
+    } while (0)
     if (dtype == kBF16) {
-        if (mode == kTileBlock) FP8Q_LAUNCH_TILE(kBF16, kTileBlock);
-        else FP8Q_LAUNCH_TILE(kBF16, kTileCols);
+        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(kBF16, kTileBlock);
+        else FP8Q_LAUNCH_TILE_RULE(kBF16, kTileCols);
     } else {
-        if (mode == kTileBlock) FP8Q_LAUNCH_TILE(kF32, kTileBlock);
-        else FP8Q_LAUNCH_TILE(kF32, kTileCols);
+        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(kF32, kTileBlock);
+        else FP8Q_LAUNCH_TILE_RULE(kF32, kTileCols);
     }
+#undef FP8Q_LAUNCH_TILE_RULE
 #undef FP8Q_LAUNCH_TILE
     return hipGetLastError();
 }

@@ -44,6 +44,12 @@ def _load_library():
     lib.fp8_grouped_gemm.restype = I
     lib.fp8_grouped_gemm.argtypes = [P, I64, P, I64, P, I64, P, P, I64, I64, P, I, I64, I64,
                                      I64, P]
+    for name, base in (("fp8_quant_1x128_pow2", "fp8_quant_1x128"),
+                       ("fp8_quant_128x128_pow2", "fp8_quant_128x128"),
+                       ("fp8_blockscaled_gemm_pow2", "fp8_blockscaled_gemm"),
+                       ("fp8_grouped_gemm_pow2", "fp8_grouped_gemm")):
+        getattr(lib, name).restype = I
+        getattr(lib, name).argtypes = getattr(lib, base).argtypes
     lib.fp8_dispatch_rows.restype = I
     lib.fp8_dispatch_rows.argtypes = [P, I64, P, I64, I64, P, I64, I64, P, I64, P, I64, P]
     lib.fp8q_status_string.restype = ctypes.c_char_p
@@ -94,7 +100,7 @@ def _require_cuda(*ts):
 # --- quantization -------------------------------------------------------------
 
 def fp8_quant_1x128(x: torch.Tensor, transposed: bool = False, q: torch.Tensor | None = None,
-                    s: torch.Tensor | None = None):
+                    s: torch.Tensor | None = None, pow2: bool = False):
     """1x128 tile quantization of a 2-D activation tensor (bf16 or fp32).
 
     transposed=False: groups of 128 along dim 1; returns q [R, C] uint8 codes
@@ -102,38 +108,41 @@ def fp8_quant_1x128(x: torch.Tensor, transposed: bool = False, q: torch.Tensor |
     transposed=True: groups of 128 along dim 0 (128x1 on the stored tensor,
     for the weight-gradient GEMM); returns the codes of x^T, q [C, R], and
     s [ceil(R/128), C].
+    pow2=True calls fp8_quant_1x128_pow2 (power-of-two scales).
     """
     _require_cuda(x)
     if x.dim() != 2:
         raise ValueError("x must be 2-D")
     R, C = x.shape
+    # a size-1 dimension may carry any stride; it is never stepped over
+    if x.stride(1) != 1 and C != 1:
+        raise ValueError("x must be contiguous along dim 1")
+    ld = x.stride(0) if R != 1 else C
     if not transposed:
-        if x.stride(1) != 1:
-            raise ValueError("x must be contiguous along dim 1")
-        rows, cols, xs_r, xs_c = R, C, x.stride(0), 1
+        rows, cols, xs_r, xs_c = R, C, ld, 1
     else:
-        if x.stride(1) != 1:
-            raise ValueError("x must be contiguous along dim 1")
-        rows, cols, xs_r, xs_c = C, R, 1, x.stride(0)
+        rows, cols, xs_r, xs_c = C, R, 1, ld
     g = (cols + 127) // 128
     if q is None:
         q = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
     if s is None:
         s = torch.empty((g, rows), dtype=torch.float32, device=x.device)
     _require_cuda(q, s)
-    st = _lib.fp8_quant_1x128(_ptr(x), _dtype_code(x), rows, cols, xs_r, xs_c, _ptr(q),
-                              q.stride(0), _ptr(s), s.stride(0), _stream(x))
-    _check(st, "fp8_quant_1x128")
+    fn = _lib.fp8_quant_1x128_pow2 if pow2 else _lib.fp8_quant_1x128
+    st = fn(_ptr(x), _dtype_code(x), rows, cols, xs_r, xs_c, _ptr(q), q.stride(0), _ptr(s),
+            s.stride(0), _stream(x))
+    _check(st, "fp8_quant_1x128" + ("_pow2" if pow2 else ""))
     return q, s
 
 
 def fp8_quant_128x128(w: torch.Tensor, with_transpose: bool = False,
                       q: torch.Tensor | None = None, s: torch.Tensor | None = None,
-                      q_t: torch.Tensor | None = None):
+                      q_t: torch.Tensor | None = None, pow2: bool = False):
     """128x128 block quantization of a 2-D weight (bf16 or fp32).
 
     Returns q [R, C] codes, s [ceil(R/128), ceil(C/128)] scales and, if
-    requested, the transposed codes q_t [C, R]."""
+    requested, the transposed codes q_t [C, R].  pow2=True calls
+    fp8_quant_128x128_pow2 (power-of-two scales)."""
     _require_cuda(w)
     if w.dim() != 2 or w.stride(1) != 1:
         raise ValueError("w must be 2-D and contiguous along dim 1")
@@ -148,10 +157,10 @@ def fp8_quant_128x128(w: torch.Tensor, with_transpose: bool = False,
     _require_cuda(q, s, q_t)
     if not s.is_contiguous():
         raise ValueError("s must be contiguous")
-    st = _lib.fp8_quant_128x128(_ptr(w), _dtype_code(w), R, C, w.stride(0), _ptr(q), q.stride(0),
-                                _ptr(s), _ptr(q_t), q_t.stride(0) if q_t is not None else 0,
-                                _stream(w))
-    _check(st, "fp8_quant_128x128")
+    fn = _lib.fp8_quant_128x128_pow2 if pow2 else _lib.fp8_quant_128x128
+    st = fn(_ptr(w), _dtype_code(w), R, C, w.stride(0), _ptr(q), q.stride(0), _ptr(s), _ptr(q_t),
+            q_t.stride(0) if q_t is not None else 0, _stream(w))
+    _check(st, "fp8_quant_128x128" + ("_pow2" if pow2 else ""))
     return q, s, q_t
 
 
@@ -176,13 +185,14 @@ def _alloc_out(M: int, N: int, dtype, device) -> torch.Tensor:
 
 def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb: torch.Tensor,
                          out_dtype=torch.bfloat16, scale_mode: int = SCALE_BLOCK128,
-                         c: torch.Tensor | None = None):
+                         c: torch.Tensor | None = None, pow2: bool = False):
     """C = A * B^T with per-128-K promotion.
 
     a [M, K] and b [N, K] uint8 E4M3 codes (K contiguous); sa [K/128, M]
     (any row pitch); sb: SCALE_BLOCK128 -> 2-D [ceil(N/128), K/128] (any
     strides, e.g. a transposed view); SCALE_ROW128 -> [K/128, N] (row pitch
-    >= N)."""
+    >= N).  pow2=True calls fp8_blockscaled_gemm_pow2 (power-of-two scales
+    applied by the matrix instruction)."""
     _require_cuda(a, sa, b, sb)
     M, K = a.shape
     N = b.shape[0]
@@ -201,21 +211,21 @@ def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb:
     _require_cuda(c)
     if c.stride(1) != 1:
         raise ValueError("c must be contiguous along dim 1")
-    st = _lib.fp8_blockscaled_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b),
-                                   b.stride(0), _ptr(sb), scale_mode, sbs0, sbs1, _ptr(c),
-                                   _out_code(c.dtype), c.stride(0), M, N, K, _stream(a))
-    _check(st, "fp8_blockscaled_gemm")
+    fn = _lib.fp8_blockscaled_gemm_pow2 if pow2 else _lib.fp8_blockscaled_gemm
+    st = fn(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb),
+            scale_mode, sbs0, sbs1, _ptr(c), _out_code(c.dtype), c.stride(0), M, N, K, _stream(a))
+    _check(st, "fp8_blockscaled_gemm" + ("_pow2" if pow2 else ""))
     return c
 
 
 def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: torch.Tensor,
                      offsets: torch.Tensor, out_dtype=torch.bfloat16,
-                     c: torch.Tensor | None = None):
+                     c: torch.Tensor | None = None, pow2: bool = False):
     """Per-group GEMM: rows [offsets[g], offsets[g+1]) of A times W_g^T.
 
     a [M_total, K] codes, sa [K/128, M_total]; w [G, N, K] codes (contiguous
     per group), sw [G, ceil(N/128), K/128] contiguous; offsets int32 [G+1] on
-    the device."""
+    the device.  pow2=True calls fp8_grouped_gemm_pow2."""
     _require_cuda(a, sa, w, sw, offsets)
     M, K = a.shape
     G, N, K2 = w.shape
@@ -227,10 +237,10 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: tor
         raise ValueError("offsets must be int32 [G+1]")
     if c is None:
         c = _alloc_out(M, N, out_dtype, a.device)
-    st = _lib.fp8_grouped_gemm(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(w),
-                               w.stride(1), _ptr(sw), _ptr(offsets), G, M, _ptr(c),
-                               _out_code(c.dtype), c.stride(0), N, K, _stream(a))
-    _check(st, "fp8_grouped_gemm")
+    fn = _lib.fp8_grouped_gemm_pow2 if pow2 else _lib.fp8_grouped_gemm
+    st = fn(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(w), w.stride(1), _ptr(sw),
+            _ptr(offsets), G, M, _ptr(c), _out_code(c.dtype), c.stride(0), N, K, _stream(a))
+    _check(st, "fp8_grouped_gemm" + ("_pow2" if pow2 else ""))
     return c
 
 

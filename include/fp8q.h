@@ -173,6 +173,43 @@ int fp8_grouped_gemm(const uint8_t* a, int64_t lda, const float* sa, int64_t lds
                      hipStream_t stream);
 
 /*
+ * Power-of-two (E8M0) scale variant.  The pages ask for matrix hardware that
+ * takes the fine-grained group scales and applies them inside the multiply,
+ * instead of promoting partial sums (why-be.why-be.co.kr page,
+ * hardware-design passage).  gfx950's scaled FP8 matrix instruction does
+ * this, with scales that are exponents only (E8M0).  The four calls below
+ * are the same operations as their FP32-scale counterparts, with:
+ *   - quantizers: each group's scale is s = 2^e, e the smallest integer with
+ *     amax <= 448 * 2^e, clamped to [-127, 127] (an all-zero group gets
+ *     2^-127), and the codes are encode(x * 2^-e) (exact scaling, then the
+ *     same round-to-nearest-even saturating E4M3 encoding).  Scales are still
+ *     stored as FP32 values, in the same layouts;
+ *   - GEMMs: every A and B scale must be such a power of two (the mantissa
+ *     bits of each scale are ignored).  The matrix instruction applies them
+ *     per 32-wide K group and accumulates across K blocks in its FP32
+ *     accumulator: no separate promotion step.  Result: sum over kb of
+ *     (sa*sb) * P_kb as for fp8_blockscaled_gemm.
+ * Arguments, layouts, alignment and error statuses are those of the
+ * corresponding call above.
+ */
+int fp8_quant_1x128_pow2(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                         int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq,
+                         float* s, int64_t lds, hipStream_t stream);
+int fp8_quant_128x128_pow2(const void* w, int w_dtype, int64_t rows, int64_t cols,
+                           int64_t ldw, uint8_t* q, int64_t ldq, float* s,
+                           uint8_t* q_t, int64_t ldqt, hipStream_t stream);
+int fp8_blockscaled_gemm_pow2(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                              const uint8_t* b, int64_t ldb, const float* sb,
+                              int b_scale_mode, int64_t sbs0, int64_t sbs1,
+                              void* c, int c_dtype, int64_t ldc,
+                              int64_t M, int64_t N, int64_t K, hipStream_t stream);
+int fp8_grouped_gemm_pow2(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa,
+                          const uint8_t* b, int64_t ldb, const float* sb,
+                          const int32_t* offsets, int64_t num_groups, int64_t M_total,
+                          void* c, int c_dtype, int64_t ldc, int64_t N, int64_t K,
+                          hipStream_t stream);
+
+/*
  * fp8_dispatch_rows -- FP8 dispatch permutation.  The activations of the MoE
  * up-projection are quantized once per token and dispatched to the experts
  * in FP8, with their scales (jp-study.kr page, passage on quantizing before

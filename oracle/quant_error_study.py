@@ -66,6 +66,16 @@ def e4m3_rows_fast(x32: np.ndarray, gc: int) -> np.ndarray:
     return e4m3_groups(x32, 1, gc)
 
 
+def e4m3_pow2(x32: np.ndarray, block: bool) -> np.ndarray:
+    """The method's groups with power-of-two (E8M0) scales (oracle rule)."""
+    if block:
+        q, s, _ = oracle.quant_128x128(x32, rule=oracle.RULE_POW2)
+        sc = np.repeat(np.repeat(s.astype(np.float64), 128, axis=0), 128, axis=1)
+        return oracle.e4m3_decode(q) * sc[:x32.shape[0], :x32.shape[1]]
+    q, s = oracle.quant_1x128(x32, rule=oracle.RULE_POW2)
+    return oracle.e4m3_decode(q) * np.repeat(s.T.astype(np.float64), 128, axis=1)[:, :x32.shape[1]]
+
+
 def e5m2_groups(x32: np.ndarray, gr: int, gc: int) -> np.ndarray:
     import torch
     R, C = x32.shape
@@ -108,7 +118,8 @@ def main():
 
     acts = {"per-tensor E4M3": e4m3_groups(a32, 0, 0),
             "per-row (1xK) E4M3": e4m3_groups(a32, 1, 0),
-            "1x128 E4M3 (method)": e4m3_rows_fast(a32, 128)}
+            "1x128 E4M3 (method)": e4m3_rows_fast(a32, 128),
+            "1x128 E4M3, power-of-two scales": e4m3_pow2(a32, False)}
     # a harder activation: the same values with per-token magnitudes spread
     # over e^[-4, 4] (seeded), as between tokens of different norm
     spread = np.exp(np.random.default_rng(11).uniform(-4.0, 4.0, (R, 1))).astype(np.float32)
@@ -119,7 +130,8 @@ def main():
               "per-row (1xK) E4M3": e4m3_groups(as32, 1, 0),
               "1x128 E4M3 (method)": e4m3_rows_fast(as32, 128)}
     wts = {"per-tensor E4M3": e4m3_groups(w32, 0, 0),
-           "128x128 E4M3 (method)": e4m3_groups(w32, 128, 128)}
+           "128x128 E4M3 (method)": e4m3_groups(w32, 128, 128),
+           "128x128 E4M3, power-of-two scales": e4m3_pow2(w32, True)}
     grads = {"per-tensor E4M3": e4m3_groups(dy32, 0, 0),
              "per-tensor E5M2": e5m2_groups(dy32, 0, 0),
              "1x128 E4M3 (method)": e4m3_rows_fast(dy32, 128),
@@ -145,6 +157,8 @@ def main():
     both = rel(acts["per-tensor E4M3"] @ wts["per-tensor E4M3"].T, c_f)
     print(f"| A, W | both per-tensor E4M3 | | | {both:.3e} |")
     print(f"| A, W | 1x128 / 128x128 (method) | | | {rel(aq @ wq.T, c_f):.3e} |")
+    p2 = rel(acts["1x128 E4M3, power-of-two scales"] @ wts["128x128 E4M3, power-of-two scales"].T, c_f)
+    print(f"| A, W | 1x128 / 128x128, power-of-two scales | | | {p2:.3e} |")
 
 
 if __name__ == "__main__":

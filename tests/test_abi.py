@@ -144,3 +144,15 @@ def test_dispatch_rows_validation(lib):
     assert disp(lib, lds_s=99) == EINVAL and disp(lib, lds_d=299) == EINVAL
     assert disp(lib, ss=A + 2) == EALIGN and disp(lib, sd=A + 1) == EALIGN
     assert disp(lib, idx=A + 2) == EALIGN
+
+
+def test_pow2_variants_validate_like_their_counterparts(lib):
+    assert lib.fp8_quant_1x128_pow2(A, 1, 4, 256, 256, 1, A, 255, A, 4, None) == EINVAL
+    assert lib.fp8_quant_1x128_pow2(A, 1, 0, 256, 256, 1, A, 256, A, 4, None) == OK
+    assert lib.fp8_quant_128x128_pow2(A, 1, 4, 256, 256, A, 256, A + 2, None, 0, None) == EALIGN
+    assert lib.fp8_blockscaled_gemm_pow2(A, 256, A, 256, A, 512, A, 0, 4, 1, A, 1, 256, 256, 256,
+                                         512, None) == EINVAL                   # lda < K
+    assert lib.fp8_blockscaled_gemm_pow2(A, 512, A, 256, A, 512, A, 0, 4, 1, A, 1, 256, 256, 256,
+                                         500, None) == EUNSUPPORTED
+    assert lib.fp8_grouped_gemm_pow2(A, 512, A, 256, A, 512, A, None, 4, 256, A, 1, 256, 256, 512,
+                                     None) == EINVAL
