@@ -14,6 +14,10 @@
 // partial-sum register set and independent VALU FMAs fold the previous
 // partial into the FP32 accumulator while the next MFMA runs.
 //
+// Two schedules share the building blocks below: the dense BLOCK128 GEMM
+// (Fprop, Dgrad) runs the ping-pong kernel gemm_pp_kernel, the ROW128 GEMM
+// (Wgrad) and the grouped GEMM the single-phase gemm_kernel.
+//
 // Design (one workgroup = one 256x256 output tile, 8 waves, 2 per SIMD):
 //  * K step 128 = exactly one scale block, so each K step is one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 output block (scale
@@ -177,6 +181,30 @@ __device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const 
         a[1] = fmaf(pp[1], sci * sbq.y, a[1]);
         a[2] = fmaf(pp[2], sci * sbq.z, a[2]);
         a[3] = fmaf(pp[3], sci * sbq.w, a[3]);
+    }
+}
+
+// Stores a lane's four consecutive outputs C[m, n..n+3] (columns < N).
+template <int OUT>
+__device__ __forceinline__ void store_out(const GemmParams& p, int64_t m, int64_t n, int64_t N,
+                                          const v4f& v) {
+    if (OUT == kF32) {
+        float* cp = static_cast<float*>(p.c) + m * p.ldc + n;
+        if (n + 4 <= N) {
+            *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+            for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
+        }
+    } else {
+        uint16_t* cp = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
+        const uint32_t h0 = float_to_bf16_bits(v[0]), h1 = float_to_bf16_bits(v[1]);
+        const uint32_t h2 = float_to_bf16_bits(v[2]), h3 = float_to_bf16_bits(v[3]);
+        if (n + 4 <= N) {
+            *reinterpret_cast<uint2*>(cp) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        } else {
+            const uint32_t h[4] = {h0, h1, h2, h3};
+            for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = (uint16_t)h[e];
+        }
     }
 }
 
@@ -445,25 +473,229 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         for (int j = 0; j < 8; ++j) {
             const int64_t n = n0 + wn * kWaveN + j * 16 + kq * 4;
             if (n >= N) continue;
-            const v4f v = acc[i][j];
-            if (OUT == kF32) {
-                float* cp = static_cast<float*>(p.c) + m * p.ldc + n;
-                if (n + 4 <= N) {
-                    *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
-                } else {
-                    for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
-                }
-            } else {
-                uint16_t* cp = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
-                const uint32_t h0 = float_to_bf16_bits(v[0]), h1 = float_to_bf16_bits(v[1]);
-                const uint32_t h2 = float_to_bf16_bits(v[2]), h3 = float_to_bf16_bits(v[3]);
-                if (n + 4 <= N) {
-                    *reinterpret_cast<uint2*>(cp) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-                } else {
-                    const uint32_t h[4] = {h0, h1, h2, h3};
-                    for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = (uint16_t)h[e];
+            store_out<OUT>(p, m, n, N, acc[i][j]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Ping-pong schedule for the dense BLOCK128 GEMM (Fprop, Dgrad).
+//
+// The two waves that share a SIMD belong to different groups: waves 0-3
+// (group 0) own the tile's output columns 0-127, waves 4-7 (group 1) columns
+// 128-255.  The groups alternate between a memory slot -- LDS fragment reads
+// and issuing the global -> LDS copies of later K steps -- and a compute slot
+// -- 16 matrix instructions on register-resident fragments, with their
+// promotions -- and every slot ends at a workgroup barrier.  On each SIMD one
+// wave therefore feeds the matrix pipe while the other one is held up by
+// memory traffic; in the single-phase kernel both waves stall on their
+// copies at the same time.  A wave runs, per K step kb,
+//   MEM(kb,0)  A fragments, B fragments of column blocks 0-3, the scales;
+//              issues the copies of its own 32 B rows of step kb+1 (into
+//              stage kb+1, whose B rows its group finished reading two
+//              slots earlier)
+//   COMP(kb,0) column blocks 0-3
+//   MEM(kb,1)  B fragments of column blocks 4-7; issues the copies of its
+//              32 A rows and its scale copy of step kb+2 (into stage kb,
+//              whose A rows and scales both groups have read by then)
+//   COMP(kb,1) column blocks 4-7
+// with group 1 one slot behind group 0.  Every copy is issued at least four
+// slots before its first reader; each wave waits for its own copies with a
+// counted vmcnt before the barrier that publishes them:
+//   group 0, after COMP(kb,1): vmcnt(5) -- all but the 5 copies of step kb+3
+//     (4 A rows + 1 scale) issued in MEM(kb,1) have landed: step kb+1's A
+//     rows, scales and B rows are complete for MEM(kb+1,0);
+//   group 1, after MEM(kb,1):  vmcnt(9) -- its A rows and scale of step kb+1
+//     have landed (its 4 B copies of step kb+1 and 5 copies of step kb+2 may
+//     still fly) before group 0 reads step kb+1 in the next slot;
+//   group 1, after COMP(kb,1): vmcnt(5) -- its B rows of step kb+1 too.
+// Results are bitwise identical to the single-phase kernel: every
+// accumulator sees the same operations in the same order.
+// ---------------------------------------------------------------------------
+
+// Slot boundaries.  The scheduling barriers keep instructions (the matrix
+// instructions included, which have no memory effects) inside their slot.
+__device__ __forceinline__ void slot_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void slot_barrier_vm5() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void slot_barrier_vm9() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int OUT, bool POW2>
+__global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
+    // [stage][0..255]: sa of the tile's rows; [stage][256 + g]: the weight
+    // block scale of column half g (fetched by the 64 lanes, lane l holding
+    // block n0/128 + (l & 1))
+    __shared__ __attribute__((aligned(16))) float smem_s[2][BM + BN];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int wm = wave & 3;       // wave row (64 rows each)
+    const int g = wave >> 2;       // group == wave column (128 columns each)
+    const int r16 = lane & 15;
+    const int kq = lane >> 4;
+
+    const int64_t N = p.N;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles_m = (p.M + BM - 1) / BM;
+    const int64_t T = tiles_m * tiles_n;
+    int64_t t = blockIdx.x;
+    if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // contiguous range per XCD
+    const int64_t grp = t / (kGroupM * tiles_n);
+    const int64_t first_m = grp * kGroupM;
+    const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
+    const int64_t rem = t - grp * kGroupM * tiles_n;
+    int64_t m0 = (first_m + rem % gm) * BM;
+    const int64_t n0 = (rem / gm) * BN;
+    const int64_t m_end = p.M;
+    const int nkb = (int)(p.K / BK);
+    const int64_t nb_last = (N + 127) / 128 - 1;
+
+    m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)m0) |
+         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)m0 >> 32)) << 32);
+    // Copy sources as in the single-phase kernel: copy qd of wave w moves
+    // rows 8*(4w+qd) .. +7 of a slab (group 0: B rows 0-127, group 1:
+    // 128-255); rows past the tile's end are clamped.
+    LoadCtx lc;
+    lc.a_base = uniform_ptr(p.a + m0 * p.lda);
+    lc.b_base = uniform_ptr(p.b + n0 * p.ldb);
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+        const int row = (wave * 4 + qd) * 8 + (lane >> 3);
+        const uint32_t kbyte = (uint32_t)(swz(row, lane & 7) * 16);
+        lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + kbyte;
+        lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
+    }
+    if (g == 1) {
+        lc.s_base = uniform_ptr(p.sb);
+        lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
+        lc.s_kstride = p.sbs1;
+    } else {
+        lc.s_base = uniform_ptr(p.sa + m0);
+        lc.s_off = (uint32_t)(min(m0 + wm * 64 + lane, m_end - 1) - m0) * 4u;
+        lc.s_kstride = p.ldsa;
+    }
+    const int s_half = g == 1 ? BM : 0;
+    auto stage_a = [&](int st) { return smem_ab[st]; };
+    auto stage_b = [&](int st) { return smem_ab[st] + kSlabBytes; };
+    auto stage_s = [&](int st) { return &smem_s[st][s_half]; };
+    // copy instructions q0 .. q1-1 (0-3 A rows, 4-7 B rows, 8 scales) of step kb
+    auto copies = [&](int q0, int q1, int kb, int st) {
+        const int kbc = kb < nkb ? kb : nkb - 1;   // past the end: harmless refill
+#pragma unroll
+        for (int q = 0; q < 9; ++q)
+            if (q >= q0 && q < q1)
+                issue_copy(q, lc, (int64_t)kbc * BK, kbc, stage_a(st), stage_b(st), stage_s(st),
+                           wave);
+    };
+
+    v4f acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+    v8i af[4], bf[4];
+    float sc[4];
+    uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of the sa rows and of sb
+
+    // COMP(kb,h): the 16 blocks (i, 4h+jj).  FP32 scales: each partial sum is
+    // promoted two instructions after it was issued (its latency).
+    auto comp = [&](int h) {
+        if constexpr (POW2) {
+#pragma unroll
+            for (int tt = 0; tt < 16; ++tt)
+                acc[tt >> 2][4 * h + (tt & 3)] = mfma_f8_scaled(
+                    bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)], sbb, sab[tt >> 2]);
+        } else {
+            v4f part[4];
+#pragma unroll
+            for (int tt = 0; tt < 18; ++tt) {
+                if (tt < 16) part[tt & 3] = mfma_f8(bf[tt & 3], af[tt >> 2]);
+                if (tt >= 2) {
+                    const int u = tt - 2;
+                    promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u & 3], sc[u >> 2],
+                                            make_float4(1.f, 1.f, 1.f, 1.f));
                 }
             }
+        }
+        // pins the half's accumulators here, so that none of the slot's
+        // (memory-free) instructions is sunk past its closing barrier
+        const int j0 = 4 * h;
+        asm volatile("" : "+v"(acc[0][j0]), "+v"(acc[0][j0 + 1]), "+v"(acc[0][j0 + 2]),
+                          "+v"(acc[0][j0 + 3]), "+v"(acc[1][j0]), "+v"(acc[1][j0 + 1]),
+                          "+v"(acc[1][j0 + 2]), "+v"(acc[1][j0 + 3]), "+v"(acc[2][j0]),
+                          "+v"(acc[2][j0 + 1]), "+v"(acc[2][j0 + 2]), "+v"(acc[2][j0 + 3]),
+                          "+v"(acc[3][j0]), "+v"(acc[3][j0 + 1]), "+v"(acc[3][j0 + 2]),
+                          "+v"(acc[3][j0 + 3]));
+    };
+
+    // prologue: step 0 complete; step 1's A rows and scales (its B rows
+    // come with MEM(0,0))
+    copies(0, 9, 0, 0);
+    copies(0, 4, 1, 1);
+    copies(8, 9, 1, 1);
+    stage_barrier();
+    if (g == 1) slot_barrier();      // group 1 starts one slot later
+
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int cur = kb & 1;
+        {   // MEM(kb,0)
+            const uint8_t* sa_ = stage_a(cur);
+            const uint8_t* sb_ = stage_b(cur);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + j, lane);
+            if constexpr (POW2) {
+                sbb = e8m0_of(smem_s[cur][BM + g]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur][wm * kWaveM + i * 16 + r16]);
+            } else {
+                const float sbv = smem_s[cur][BM + g];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16] * sbv;
+            }
+            copies(4, 8, kb + 1, cur ^ 1);
+        }
+        slot_barrier();
+        comp(0);
+        slot_barrier();
+        {   // MEM(kb,1)
+            const uint8_t* sb_ = stage_b(cur);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + 4 + j, lane);
+            copies(0, 4, kb + 2, cur);
+            copies(8, 9, kb + 2, cur);
+        }
+        if (g == 1) slot_barrier_vm9(); else slot_barrier();
+        comp(1);
+        slot_barrier_vm5();
+    }
+    if (g == 0) slot_barrier();      // group 0's idle last slot
+    wait_vm_all();
+
+    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 block ----
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + wm * kWaveM + i * 16 + r16;
+        if (m >= m_end) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t n = n0 + g * kWaveN + j * 16 + kq * 4;
+            if (n >= N) continue;
+            store_out<OUT>(p, m, n, N, acc[i][j]);
         }
     }
 }
@@ -472,22 +704,25 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
                        hipStream_t stream) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
-#define FP8Q_GEMM(SM, OD, P2) \
-    hipLaunchKernelGGL((gemm_kernel<SM, OD, false, P2>), grid, block, 0, stream, p)
-#define FP8Q_GEMM_P2(SM, OD)                  \
-    do {                                      \
-        if (pow2) FP8Q_GEMM(SM, OD, true);    \
-        else FP8Q_GEMM(SM, OD, false);        \
-    } while (0)
     if (scale_mode == kScaleBlock128) {
-        if (out_dtype == kBF16) FP8Q_GEMM_P2(kScaleBlock128, kBF16);
-        else FP8Q_GEMM_P2(kScaleBlock128, kF32);
-    } else {
-        if (out_dtype == kBF16) FP8Q_GEMM_P2(kScaleRow128, kBF16);
-        else FP8Q_GEMM_P2(kScaleRow128, kF32);
+        // dense Fprop / Dgrad: ping-pong schedule
+        if (out_dtype == kBF16) {
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false>), grid, block, 0, stream, p);
+        } else {
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false>), grid, block, 0, stream, p);
+        }
+        return hipGetLastError();
     }
-#undef FP8Q_GEMM_P2
-#undef FP8Q_GEMM
+    // ROW128 (Wgrad): single-phase kernel
+    if (out_dtype == kBF16) {
+        if (pow2) hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kBF16, false, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kBF16, false, false>), grid, block, 0, stream, p);
+    } else {
+        if (pow2) hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kF32, false, true>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kF32, false, false>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 
