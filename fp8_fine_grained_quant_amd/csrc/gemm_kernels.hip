@@ -14,9 +14,9 @@
 // partial-sum register set and independent VALU FMAs fold the previous
 // partial into the FP32 accumulator while the next MFMA runs.
 //
-// Two schedules share the building blocks below: the dense BLOCK128 GEMM
-// (Fprop, Dgrad) runs the ping-pong kernel gemm_pp_kernel, the ROW128 GEMM
-// (Wgrad) and the grouped GEMM the single-phase gemm_kernel.
+// Two schedules share the building blocks below: the BLOCK128 GEMMs (Fprop,
+// Dgrad, the grouped MoE GEMM) run the ping-pong kernel gemm_pp_kernel, the
+// ROW128 GEMM (Wgrad) the single-phase gemm_kernel.
 //
 // Design (one workgroup = one 256x256 output tile, 8 waves, 2 per SIMD):
 //  * K step 128 = exactly one scale block, so each K step is one
@@ -184,6 +184,78 @@ __device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const 
     }
 }
 
+// The output tile of this workgroup.  Dense: blockIdx -> (m0, n0) with each
+// XCD on a contiguous range of tiles, walked in groups of kGroupM tile rows.
+// Grouped: a tile table built in LDS -- group g owns tiles [tile_start[g],
+// tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them, in (m-tile, n-tile)
+// order -- and a binary search; returns false (for the whole workgroup) past
+// the last tile.  bptr / sbptr are advanced to the group's weight and scales.
+template <bool GROUPED>
+__device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_start,
+                                            int32_t* wave_tot, int tid, int lane, int wave,
+                                            int64_t& m0, int64_t& m_end, int64_t& n0,
+                                            const uint8_t*& bptr, const float*& sbptr) {
+    const int64_t N = p.N;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    if (!GROUPED) {
+        const int64_t tiles_m = (p.M + BM - 1) / BM;
+        const int64_t T = tiles_m * tiles_n;
+        int64_t t = blockIdx.x;
+        if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // contiguous range per XCD
+        const int64_t grp = t / (kGroupM * tiles_n);
+        const int64_t first_m = grp * kGroupM;
+        const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
+        const int64_t rem = t - grp * kGroupM * tiles_n;
+        m0 = (first_m + rem % gm) * BM;
+        n0 = (rem / gm) * BN;
+        m_end = p.M;
+        return true;
+    }
+    const int64_t G = p.num_groups;
+    const int per = (int)((G + kThreads - 1) / kThreads);
+    const int g0 = tid * per;
+    int32_t local = 0;
+    for (int g = g0; g < g0 + per && g < G; ++g) {
+        const int32_t rows = p.offsets[g + 1] - p.offsets[g];
+        local += (rows + BM - 1) / BM * (int32_t)tiles_n;
+    }
+    int32_t incl = local;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        int32_t v = __shfl_up(incl, d);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int32_t base = 0;
+    for (int w = 0; w < wave; ++w) base += wave_tot[w];
+    int32_t run = base + incl - local;
+    for (int g = g0; g < g0 + per && g < G; ++g) {
+        tile_start[g] = run;
+        const int32_t rows = p.offsets[g + 1] - p.offsets[g];
+        run += (rows + BM - 1) / BM * (int32_t)tiles_n;
+    }
+    if (tid == kThreads - 1) tile_start[G] = run;
+    __syncthreads();
+    const int32_t t = (int32_t)blockIdx.x;
+    if (t >= tile_start[G]) return false;
+    int lo = 0, hi = (int)G;         // tile_start[lo] <= t < tile_start[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (tile_start[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int g = lo;
+    const int32_t local_t = t - tile_start[g];
+    const int64_t tm = local_t / tiles_n;
+    const int64_t tn = local_t - tm * tiles_n;
+    m0 = p.offsets[g] + tm * BM;
+    m_end = p.offsets[g + 1];
+    n0 = tn * BN;
+    bptr += (int64_t)g * N * p.ldb;
+    sbptr += (int64_t)g * ((N + 127) / 128) * (p.K / 128);
+    return true;
+}
+
 // Stores a lane's four consecutive outputs C[m, n..n+3] (columns < N).
 template <int OUT>
 __device__ __forceinline__ void store_out(const GemmParams& p, int64_t m, int64_t n, int64_t N,
@@ -226,68 +298,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     const int64_t N = p.N;
     const int64_t tiles_n = (N + BN - 1) / BN;
-    const uint8_t* __restrict__ bptr = p.b;
-    const float* __restrict__ sbptr = p.sb;
+    const uint8_t* bptr = p.b;
+    const float* sbptr = p.sb;
     int64_t m0, m_end, n0;
 
-    if (!GROUPED) {
-        const int64_t tiles_m = (p.M + BM - 1) / BM;
-        const int64_t T = tiles_m * tiles_n;
-        int64_t t = blockIdx.x;
-        if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // contiguous range per XCD
-        const int64_t grp = t / (kGroupM * tiles_n);
-        const int64_t first_m = grp * kGroupM;
-        const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
-        const int64_t rem = t - grp * kGroupM * tiles_n;
-        m0 = (first_m + rem % gm) * BM;
-        n0 = (rem / gm) * BN;
-        m_end = p.M;
-    } else {
-        // Tile table: group g owns tiles [tile_start[g], tile_start[g+1]),
-        // ceil(rows_g/BM) * tiles_n of them, in (m-tile, n-tile) order.
-        const int64_t G = p.num_groups;
-        const int per = (int)((G + kThreads - 1) / kThreads);
-        const int g0 = tid * per;
-        int32_t local = 0;
-        for (int g = g0; g < g0 + per && g < G; ++g) {
-            const int32_t rows = p.offsets[g + 1] - p.offsets[g];
-            local += (rows + BM - 1) / BM * (int32_t)tiles_n;
-        }
-        int32_t incl = local;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            int32_t v = __shfl_up(incl, d);
-            if (lane >= d) incl += v;
-        }
-        if (lane == 63) wave_tot[wave] = incl;
-        __syncthreads();
-        int32_t base = 0;
-        for (int w = 0; w < wave; ++w) base += wave_tot[w];
-        int32_t run = base + incl - local;
-        for (int g = g0; g < g0 + per && g < G; ++g) {
-            tile_start[g] = run;
-            const int32_t rows = p.offsets[g + 1] - p.offsets[g];
-            run += (rows + BM - 1) / BM * (int32_t)tiles_n;
-        }
-        if (tid == kThreads - 1) tile_start[G] = run;
-        __syncthreads();
-        const int32_t t = (int32_t)blockIdx.x;
-        if (t >= tile_start[G]) return;  // whole workgroup: uniform exit
-        int lo = 0, hi = (int)G;         // tile_start[lo] <= t < tile_start[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (tile_start[mid] <= t) lo = mid; else hi = mid;
-        }
-        const int g = lo;
-        const int32_t local_t = t - tile_start[g];
-        const int64_t tm = local_t / tiles_n;
-        const int64_t tn = local_t - tm * tiles_n;
-        m0 = p.offsets[g] + tm * BM;
-        m_end = p.offsets[g + 1];
-        n0 = tn * BN;
-        bptr += (int64_t)g * N * p.ldb;
-        sbptr += (int64_t)g * ((N + 127) / 128) * (p.K / 128);
-    }
+    if (!locate_tile<GROUPED>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
+        return;  // whole workgroup: uniform exit (grouped GEMM, surplus workgroup)
 
     const int nkb = (int)(p.K / BK);
     const int64_t nb_last = (N + 127) / 128 - 1;
@@ -531,13 +547,15 @@ __device__ __forceinline__ void slot_barrier_vm9() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int OUT, bool POW2>
+template <int OUT, bool POW2, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
     // [stage][0..255]: sa of the tile's rows; [stage][256 + g]: the weight
     // block scale of column half g (fetched by the 64 lanes, lane l holding
     // block n0/128 + (l & 1))
     __shared__ __attribute__((aligned(16))) float smem_s[2][BM + BN];
+    __shared__ int32_t tile_start[GROUPED ? (kMaxGroups + 1) : 1];
+    __shared__ int32_t wave_tot[kThreads / 64];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -548,18 +566,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     const int kq = lane >> 4;
 
     const int64_t N = p.N;
-    const int64_t tiles_n = (N + BN - 1) / BN;
-    const int64_t tiles_m = (p.M + BM - 1) / BM;
-    const int64_t T = tiles_m * tiles_n;
-    int64_t t = blockIdx.x;
-    if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // contiguous range per XCD
-    const int64_t grp = t / (kGroupM * tiles_n);
-    const int64_t first_m = grp * kGroupM;
-    const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
-    const int64_t rem = t - grp * kGroupM * tiles_n;
-    int64_t m0 = (first_m + rem % gm) * BM;
-    const int64_t n0 = (rem / gm) * BN;
-    const int64_t m_end = p.M;
+    const uint8_t* bptr = p.b;
+    const float* sbptr = p.sb;
+    int64_t m0, m_end, n0;
+    if (!locate_tile<GROUPED>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
+        return;  // whole workgroup: uniform exit (grouped GEMM, surplus workgroup)
     const int nkb = (int)(p.K / BK);
     const int64_t nb_last = (N + 127) / 128 - 1;
 
@@ -570,7 +581,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     // 128-255); rows past the tile's end are clamped.
     LoadCtx lc;
     lc.a_base = uniform_ptr(p.a + m0 * p.lda);
-    lc.b_base = uniform_ptr(p.b + n0 * p.ldb);
+    lc.b_base = uniform_ptr(bptr + n0 * p.ldb);
 #pragma unroll
     for (int qd = 0; qd < 4; ++qd) {
         const int row = (wave * 4 + qd) * 8 + (lane >> 3);
@@ -579,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
     }
     if (g == 1) {
-        lc.s_base = uniform_ptr(p.sb);
+        lc.s_base = uniform_ptr(sbptr);
         lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
         lc.s_kstride = p.sbs1;
     } else {
@@ -707,11 +718,11 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
     if (scale_mode == kScaleBlock128) {
         // dense Fprop / Dgrad: ping-pong schedule
         if (out_dtype == kBF16) {
-            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false>), grid, block, 0, stream, p);
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true, false>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false, false>), grid, block, 0, stream, p);
         } else {
-            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false>), grid, block, 0, stream, p);
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true, false>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false, false>), grid, block, 0, stream, p);
         }
         return hipGetLastError();
     }
@@ -730,8 +741,13 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, bool pow2, hi
     // upper bound on the tile count: sum_g ceil(rows_g/BM) <= M/BM + groups
     const int64_t tiles = ((p.M + BM - 1) / BM + p.num_groups) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
+#ifdef FP8Q_GROUPED_SINGLE_PHASE
 #define FP8Q_GGEMM(OD, P2) \
     hipLaunchKernelGGL((gemm_kernel<kScaleBlock128, OD, true, P2>), grid, block, 0, stream, p)
+#else
+#define FP8Q_GGEMM(OD, P2) \
+    hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, true>), grid, block, 0, stream, p)
+#endif
     if (out_dtype == kBF16) {
         if (pow2) FP8Q_GGEMM(kBF16, true);
         else FP8Q_GGEMM(kBF16, false);
