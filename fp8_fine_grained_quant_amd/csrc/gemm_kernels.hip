@@ -297,7 +297,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int wn = wave >> 2;  // wave column (128 columns each)
 
     const int64_t N = p.N;
-    const int64_t tiles_n = (N + BN - 1) / BN;
     const uint8_t* bptr = p.b;
     const float* sbptr = p.sb;
     int64_t m0, m_end, n0;
@@ -547,6 +546,10 @@ __device__ __forceinline__ void slot_barrier_vm9() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Distance, in matrix instructions, between a partial sum's instruction and
+// the FMAs that promote it (the partial ring holds 4).
+constexpr int kPromoteDist = 2;
+
 template <int OUT, bool POW2, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
@@ -632,14 +635,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         } else {
             v4f part[4];
 #pragma unroll
-            for (int tt = 0; tt < 18; ++tt) {
+            for (int tt = 0; tt < 16 + kPromoteDist; ++tt) {
                 if (tt < 16) part[tt & 3] = mfma_f8(bf[tt & 3], af[tt >> 2]);
-                if (tt >= 2) {
-                    const int u = tt - 2;
+                if (tt >= kPromoteDist) {
+                    const int u = tt - kPromoteDist;
                     promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u & 3], sc[u >> 2],
                                             make_float4(1.f, 1.f, 1.f, 1.f));
                 }
             }
+            // issue order pinned: kPromoteDist matrix instructions, then
+            // each further one followed by the four FMAs of an earlier
+            // partial (left to itself the scheduler packs the FMAs right
+            // behind their own instruction, into hazard wait states)
+#pragma unroll
+            for (int tt = 0; tt < kPromoteDist; ++tt) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+            for (int tt = kPromoteDist; tt < 16; ++tt) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x002, 4 * kPromoteDist, 0);
         }
         // pins the half's accumulators here, so that none of the slot's
         // (memory-free) instructions is sunk past its closing barrier
