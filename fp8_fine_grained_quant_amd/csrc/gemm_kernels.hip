@@ -547,8 +547,11 @@ __device__ __forceinline__ void slot_barrier_vm9() {
 }
 
 // Distance, in matrix instructions, between a partial sum's instruction and
-// the FMAs that promote it (the partial ring holds 4).
-constexpr int kPromoteDist = 2;
+// the FMAs that promote it, and the ring of partial sums that distance needs.
+// An FMA that reads a result still in flight holds up the wave's in-order
+// issue, and with it the matrix pipe; at distance 4 the result has landed.
+constexpr int kPromoteDist = 4;
+constexpr int kPartRing = kPromoteDist + 1;
 
 template <int OUT, bool POW2, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of the sa rows and of sb
 
     // COMP(kb,h): the 16 blocks (i, 4h+jj).  FP32 scales: each partial sum is
-    // promoted two instructions after it was issued (its latency).
+    // promoted kPromoteDist instructions after it was issued.
     auto comp = [&](int h) {
         if constexpr (POW2) {
 #pragma unroll
@@ -633,13 +636,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                 acc[tt >> 2][4 * h + (tt & 3)] = mfma_f8_scaled(
                     bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)], sbb, sab[tt >> 2]);
         } else {
-            v4f part[4];
+            v4f part[kPartRing];
 #pragma unroll
             for (int tt = 0; tt < 16 + kPromoteDist; ++tt) {
-                if (tt < 16) part[tt & 3] = mfma_f8(bf[tt & 3], af[tt >> 2]);
+                if (tt < 16) part[tt % kPartRing] = mfma_f8(bf[tt & 3], af[tt >> 2]);
                 if (tt >= kPromoteDist) {
                     const int u = tt - kPromoteDist;
-                    promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u & 3], sc[u >> 2],
+                    promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u % kPartRing], sc[u >> 2],
                                             make_float4(1.f, 1.f, 1.f, 1.f));
                 }
             }

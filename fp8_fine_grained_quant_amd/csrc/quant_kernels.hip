@@ -29,28 +29,18 @@
 
 namespace fp8q {
 
-#ifndef FP8Q_ROW_UNROLL
-#define FP8Q_ROW_UNROLL 4
-#endif
-constexpr int kRowUnroll = FP8Q_ROW_UNROLL;
+// group loads in flight per lane in the 1x128 row kernel
+constexpr int kRowUnroll = 4;
 
 // ---------------------------------------------------------------------------
 // 1x128 groups along contiguous rows
 // ---------------------------------------------------------------------------
 
-#ifndef FP8Q_NT
-#define FP8Q_NT 1
-#endif
 // Streaming 16-byte load: every input byte is read exactly once, so the
 // non-temporal hint keeps it from displacing reusable cache lines.
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
-#if FP8Q_NT
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
-#endif
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -92,22 +82,15 @@ __device__ __forceinline__ void load8(const void* row, int64_t c0, int64_t cols,
 }
 
 // Stores the 8 code bytes of [c0, c0+8) (those below `cols`); `vec`: the
-// row start is 8-byte aligned, so full runs use one 8-byte store.  STREAM:
-// non-temporal store, for outputs written in whole contiguous runs (the
-// transposed outputs are written 8 bytes per row and are better merged in
-// the cache first).
-template <bool STREAM = true>
+// row start is 8-byte aligned, so full runs use one 8-byte store.  Plain
+// (temporal) stores: the codes are read next by the GEMM, and kept in the
+// memory-side cache they need not come back from HBM (measured: the Fprop
+// GEMM after the quantizers runs ~1-2 % faster than after non-temporal
+// stores).
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c0, int64_t cols, uint32_t lo,
                                        uint32_t hi, bool vec) {
     if (vec && c0 + 8 <= cols) {
-#if FP8Q_NT
-        if (STREAM)
-            __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(row + c0));
-        else
-            *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
-#else
         *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
-#endif
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -291,7 +274,7 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
                 tlo |= code_byte(lo[p], hi[p], j) << (8 * p);
                 thi |= code_byte(lo[p + 4], hi[p + 4], j) << (8 * p);
             }
-            if (c0 + j < cols) store8<false>(qt + (c0 + j) * ldqt, r0, rows, tlo, thi, vqt);
+            if (c0 + j < cols) store8(qt + (c0 + j) * ldqt, r0, rows, tlo, thi, vqt);
         }
     }
 }
