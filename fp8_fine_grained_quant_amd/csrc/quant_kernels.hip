@@ -11,9 +11,11 @@
 // once, every output byte written once, with 16-byte vector accesses on the
 // interior and element-guarded accesses on ragged edges.
 //
-//  quant_rows_kernel  -- 1x128 groups along a contiguous row.  One 16-lane
+//  quant_rows_kernel  -- 1x128 groups along contiguous rows.  One 16-lane
 //                        DPP row per group (8 elements per lane), so the
-//                        group max is a 4-step row_ror reduction with no LDS.
+//                        group max is a 4-step row_ror reduction with no
+//                        LDS; a grid of resident waves strides over the
+//                        groups.
 //  quant_tile_kernel  -- 128x128 input tiles, thread (a, b) of 256 owning the
 //                        8x8 sub-tile rows 8a..8a+7, cols 8b..8b+7:
 //                        MODE_BLOCK: one scale per tile (weights), codes
@@ -30,7 +32,7 @@
 namespace fp8q {
 
 // group loads in flight per lane in the 1x128 row kernel
-constexpr int kRowUnroll = 4;
+constexpr int kRowUnroll = 2;
 
 // ---------------------------------------------------------------------------
 // 1x128 groups along contiguous rows
@@ -44,40 +46,50 @@ __device__ __forceinline__ uint4 ld_stream16(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// Loads the 8 elements [c0, c0+8) of a row as FP32; elements at or beyond
-// `cols` read as 0 (they do not change the group max and are not stored).
-// `vec`: the row start is 16-byte aligned, so full runs use vector loads.
+// Eight consecutive elements of a row, as raw 16-byte runs (BF16: one run,
+// FP32: two).  Loading is split from unpacking so that a thread issues all
+// of its loads before it consumes any: a load whose result is used right
+// away would make every load of the thread wait for the one before.
+struct Run8 {
+    uint4 a, b;
+};
 template <int DT>
-__device__ __forceinline__ void load8(const void* row, int64_t c0, int64_t cols, float v[8],
-                                      bool vec) {
-    if (vec && c0 + 8 <= cols) {
-        if (DT == kBF16) {
-            uint4 u = ld_stream16(static_cast<const uint16_t*>(row) + c0);
-            uint32_t w[4] = {u.x, u.y, u.z, u.w};
+__device__ __forceinline__ void issue8(const void* row, int64_t c0, Run8& r) {
+    if (DT == kBF16) {
+        r.a = ld_stream16(static_cast<const uint16_t*>(row) + c0);
+    } else {
+        const float* p = static_cast<const float*>(row) + c0;
+        r.a = ld_stream16(p);
+        r.b = ld_stream16(p + 4);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void unpack8(const Run8& r, float v[8]) {
+    if (DT == kBF16) {
+        const uint32_t w[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                v[2 * i] = bf16_bits_to_float(w[i] & 0xFFFFu);
-                v[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
-            }
-        } else {
-            const float* p = static_cast<const float*>(row) + c0;
-            const uint4 a = ld_stream16(p), b = ld_stream16(p + 4);
-            v[0] = __uint_as_float(a.x); v[1] = __uint_as_float(a.y);
-            v[2] = __uint_as_float(a.z); v[3] = __uint_as_float(a.w);
-            v[4] = __uint_as_float(b.x); v[5] = __uint_as_float(b.y);
-            v[6] = __uint_as_float(b.z); v[7] = __uint_as_float(b.w);
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_bits_to_float(w[i] & 0xFFFFu);
+            v[2 * i + 1] = bf16_bits_to_float(w[i] >> 16);
         }
     } else {
+        v[0] = __uint_as_float(r.a.x); v[1] = __uint_as_float(r.a.y);
+        v[2] = __uint_as_float(r.a.z); v[3] = __uint_as_float(r.a.w);
+        v[4] = __uint_as_float(r.b.x); v[5] = __uint_as_float(r.b.y);
+        v[6] = __uint_as_float(r.b.z); v[7] = __uint_as_float(r.b.w);
+    }
+}
+// Element-wise fallback (unaligned rows, ragged edges): [c0, c0+8) as FP32,
+// elements at or beyond `cols` read as 0 (they change neither the group
+// max nor any stored code).
+template <int DT>
+__device__ __forceinline__ void load8_elems(const void* row, int64_t c0, int64_t cols, float v[8]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int64_t c = c0 + i;
-            if (c < cols) {
-                v[i] = DT == kBF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(row)[c])
-                                   : static_cast<const float*>(row)[c];
-            } else {
-                v[i] = 0.0f;
-            }
-        }
+    for (int i = 0; i < 8; ++i) {
+        const int64_t c = c0 + i;
+        v[i] = c < cols ? (DT == kBF16 ? bf16_bits_to_float(static_cast<const uint16_t*>(row)[c])
+                                       : static_cast<const float*>(row)[c])
+                        : 0.0f;
     }
 }
 
@@ -110,45 +122,64 @@ __device__ __forceinline__ void quant_group_1x128(const float v[8], uint8_t* qro
     m = row16_max_u32(m);
     float s, inv;
     group_scale_rule<RULE>(__uint_as_float(m), s, inv);
-    uint32_t lo = enc4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
-    uint32_t hi = enc4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
+    const uint32_t lo = enc4(v[0] * inv, v[1] * inv, v[2] * inv, v[3] * inv);
+    const uint32_t hi = enc4(v[4] * inv, v[5] * inv, v[6] * inv, v[7] * inv);
     store8(qrow, c0, cols, lo, hi, vout);
     if (lead) *s_out = s;
 }
 
-// Grid: blocks of 4 waves; wave w of block b handles rows b*4+w (grid-strided);
-// within a row, the 4 DPP rows (slices) of the wave take groups g = slice,
-// slice+4, ... so one wave-load covers 4 consecutive groups (1 KB of BF16).
+// Division by a launch constant d (the groups per row) as a multiply-high:
+// n / d = (umulhi(n, m) + n) >> l for every 32-bit n, with l = ceil(log2 d)
+// and m = floor(2^32 (2^l - d) / d) + 1 (Granlund and Montgomery, "Division
+// by invariant integers using multiplication", 1994).
+struct DivMagic {
+    uint32_t m, l;
+};
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic d) {
+    return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
+}
+
+// Groups are numbered row-major, gi = r * gpr + g (gpr groups per row, fewer
+// than 2^31 per launch), so a wave streams through consecutive addresses.
+// The grid is a few resident rounds of waves striding over the groups; a
+// wave takes 4 * kRowUnroll consecutive groups per pass (slice = lane / 16
+// picks one of 4 per step), issuing all of its loads before it consumes
+// any, and every wave gets the same share however the rows fall.
 template <int DT, int RULE>
-__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t rows,
-                                                         int64_t cols, int64_t ldx,
-                                                         uint8_t* __restrict__ q, int64_t ldq,
-                                                         float* __restrict__ s, int64_t lds,
-                                                         bool vin, bool vout) {
+__global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t cols,
+                                                         int64_t ldx, uint8_t* __restrict__ q,
+                                                         int64_t ldq, float* __restrict__ s,
+                                                         int64_t lds, uint32_t total, uint32_t gpr,
+                                                         DivMagic dm, bool vin, bool vout) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int slice = lane >> 4;
     const int sl = lane & 15;
-    const int64_t groups = (cols + 127) >> 7;
     const size_t esz = DT == kBF16 ? 2 : 4;
-    for (int64_t r = (int64_t)blockIdx.x * 4 + wave; r < rows; r += (int64_t)gridDim.x * 4) {
-        const void* xr = static_cast<const char*>(x) + (size_t)r * (size_t)ldx * esz;
-        uint8_t* qr = q + r * ldq;
-        // kRowUnroll group loads in flight per lane before any is consumed
-        for (int64_t g0 = 0; g0 < groups; g0 += 4 * kRowUnroll) {
-            float v[kRowUnroll][8];
+    const uint32_t step = gridDim.x * 4u * 4u * kRowUnroll;
+    for (uint32_t base = (blockIdx.x * 4u + wave) * 4u * kRowUnroll; base < total; base += step) {
+        Run8 raw[kRowUnroll];
+        uint32_t rr[kRowUnroll], gg[kRowUnroll];
+        bool vec[kRowUnroll];
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t g = g0 + 4 * u + slice;
-                if (g < groups) load8<DT>(xr, g * 128 + sl * 8, cols, v[u], vin);
-            }
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const uint32_t gi = base + 4 * u + slice;
+            rr[u] = div_magic(gi, dm);
+            gg[u] = gi - rr[u] * gpr;
+            const int64_t c0 = (int64_t)gg[u] * 128 + sl * 8;
+            vec[u] = vin && gi < total && c0 + 8 <= cols;
+            if (vec[u]) issue8<DT>(static_cast<const char*>(x) + (size_t)rr[u] * (size_t)ldx * esz, c0, raw[u]);
+        }
 #pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int64_t g = g0 + 4 * u + slice;
-                if (g < groups)
-                    quant_group_1x128<DT, RULE>(v[u], qr, g * 128 + sl * 8, cols, s + g * lds + r, sl == 0,
-                                          vout);
-            }
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const uint32_t gi = base + 4 * u + slice;
+            if (gi >= total) continue;
+            const int64_t c0 = (int64_t)gg[u] * 128 + sl * 8;
+            float v[8];
+            if (vec[u]) unpack8<DT>(raw[u], v);
+            else load8_elems<DT>(static_cast<const char*>(x) + (size_t)rr[u] * (size_t)ldx * esz, c0, cols, v);
+            quant_group_1x128<DT, RULE>(v, q + (int64_t)rr[u] * ldq, c0, cols,
+                                        s + (int64_t)gg[u] * lds + rr[u], sl == 0, vout);
         }
     }
 }
@@ -158,19 +189,26 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 // ---------------------------------------------------------------------------
 
 // Reads the 8x8 sub-tile rows r0..r0+7, cols c0..c0+7 of a row-major matrix;
-// elements outside [rows, cols] read as 0.
+// elements outside [rows, cols] read as 0.  An interior sub-tile of an
+// aligned matrix issues its eight row loads before unpacking any.
 template <int DT>
 __device__ __forceinline__ void load_8x8(const void* x, int64_t ldx, int64_t rows, int64_t cols,
                                          int64_t r0, int64_t c0, float v[8][8], bool vin) {
     const size_t esz = DT == kBF16 ? 2 : 4;
-    const bool full = (r0 + 8 <= rows) && (c0 + 8 <= cols);
+    if (vin && r0 + 8 <= rows && c0 + 8 <= cols) {
+        Run8 raw[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            issue8<DT>(static_cast<const char*>(x) + (size_t)(r0 + p) * (size_t)ldx * esz, c0, raw[p]);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) unpack8<DT>(raw[p], v[p]);
+        return;
+    }
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-        const void* row = static_cast<const char*>(x) + (size_t)(r0 + p) * (size_t)ldx * esz;
-        if (full) {
-            load8<DT>(row, c0, cols, v[p], vin);
-        } else if (r0 + p < rows) {
-            load8<DT>(row, c0, cols, v[p], vin);
+        if (r0 + p < rows) {
+            load8_elems<DT>(static_cast<const char*>(x) + (size_t)(r0 + p) * (size_t)ldx * esz, c0,
+                            cols, v[p]);
         } else {
 #pragma unroll
             for (int j = 0; j < 8; ++j) v[p][j] = 0.0f;
@@ -287,27 +325,74 @@ static bool is_aligned(const void* p, uintptr_t a) {
     return reinterpret_cast<uintptr_t>(p) % a == 0;
 }
 
+// Resident workgroups of quant_rows_kernel<DT, RL> on the current device
+// (cached per device).
+template <int DT, int RL>
+static int64_t rows_resident_blocks() {
+    static int cached[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2048;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<DT, RL>, 256, 0) !=
+                hipSuccess ||
+            per_cu <= 0)
+            per_cu = 4;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+        cached[dev] = per_cu * cus;
+    }
+    return cached[dev];
+}
+
+static DivMagic make_div_magic(uint32_t d) {
+    uint32_t l = 0;
+    while (((uint64_t)1 << l) < d) ++l;
+    const uint64_t m = ((((uint64_t)1 << 32) * (((uint64_t)1 << l) - d)) / d) + 1;
+    return DivMagic{(uint32_t)m, l};
+}
+
+template <int DT, int RL>
+static hipError_t launch_rows_t(const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                                uint8_t* q, int64_t ldq, float* s, int64_t lds, bool vin,
+                                bool vout, hipStream_t stream) {
+    const int64_t esz = DT == kBF16 ? 2 : 4;
+    const int64_t gpr = (cols + 127) / 128;
+    if (rows <= 0 || gpr <= 0) return hipSuccess;
+    const DivMagic dm = make_div_magic((uint32_t)gpr);
+    // four resident rounds of workgroups (measured best among 1, 2, 4, 8)
+    const int64_t cap = 4 * rows_resident_blocks<DT, RL>();
+    // rows per launch: fewer than 2^31 groups, so 32-bit group indices
+    const int64_t chunk = ((int64_t)1 << 31) / gpr - 1;
+    for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
+        const int64_t nr = rows - r0 < chunk ? rows - r0 : chunk;
+        const int64_t total = nr * gpr;
+        int64_t blocks = (total + 16 * kRowUnroll - 1) / (16 * kRowUnroll);
+        if (blocks > cap) blocks = cap;
+        hipLaunchKernelGGL((quant_rows_kernel<DT, RL>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                           static_cast<const char*>(x) + r0 * ldx * esz, cols, ldx, q + r0 * ldq,
+                           ldq, s + r0, lds, (uint32_t)total, (uint32_t)gpr, dm, vin, vout);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, int rule,
                              hipStream_t stream) {
-    int64_t blocks = (rows + 3) / 4;
-    if (blocks > 65536 * 8) blocks = 65536 * 8;
-    dim3 grid((unsigned)blocks), block(256);
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vout = is_aligned(q, 8) && ldq % 8 == 0;
-#define FP8Q_LAUNCH_ROWS(DT, RL)                                                               \
-    hipLaunchKernelGGL((quant_rows_kernel<DT, RL>), grid, block, 0, stream, x, rows, cols, ldx, q, \
-                       ldq, s, lds, vin, vout)
     if (dtype == kBF16) {
-        if (rule == kRulePow2) FP8Q_LAUNCH_ROWS(kBF16, kRulePow2);
-        else FP8Q_LAUNCH_ROWS(kBF16, kRuleFP32);
-    } else {
-        if (rule == kRulePow2) FP8Q_LAUNCH_ROWS(kF32, kRulePow2);
-        else FP8Q_LAUNCH_ROWS(kF32, kRuleFP32);
+        if (rule == kRulePow2)
+            return launch_rows_t<kBF16, kRulePow2>(x, rows, cols, ldx, q, ldq, s, lds, vin, vout, stream);
+        return launch_rows_t<kBF16, kRuleFP32>(x, rows, cols, ldx, q, ldq, s, lds, vin, vout, stream);
     }
-#undef FP8Q_LAUNCH_ROWS
-    return hipGetLastError();
+    if (rule == kRulePow2)
+        return launch_rows_t<kF32, kRulePow2>(x, rows, cols, ldx, q, ldq, s, lds, vin, vout, stream);
+    return launch_rows_t<kF32, kRuleFP32>(x, rows, cols, ldx, q, ldq, s, lds, vin, vout, stream);
 }
 
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
