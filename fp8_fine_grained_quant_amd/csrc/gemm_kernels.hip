@@ -759,13 +759,8 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, bool pow2, hi
     // upper bound on the tile count: sum_g ceil(rows_g/BM) <= M/BM + groups
     const int64_t tiles = ((p.M + BM - 1) / BM + p.num_groups) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
-#ifdef FP8Q_GROUPED_SINGLE_PHASE
-#define FP8Q_GGEMM(OD, P2) \
-    hipLaunchKernelGGL((gemm_kernel<kScaleBlock128, OD, true, P2>), grid, block, 0, stream, p)
-#else
 #define FP8Q_GGEMM(OD, P2) \
     hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, true>), grid, block, 0, stream, p)
-#endif
     if (out_dtype == kBF16) {
         if (pow2) FP8Q_GGEMM(kBF16, true);
         else FP8Q_GGEMM(kBF16, false);

@@ -26,6 +26,8 @@
 //                        The transposed store is an 8x8 byte transpose in
 //                        registers, so each thread writes 8-byte runs and
 //                        the 16 threads of a column run write 128 bytes.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -327,12 +329,14 @@ static bool is_aligned(const void* p, uintptr_t a) {
 
 // Resident workgroups of quant_rows_kernel<DT, RL> on the current device
 // (cached per device).
+// Threads may race to fill an entry; they all store the same value.
 template <int DT, int RL>
 static int64_t rows_resident_blocks() {
-    static int cached[64] = {};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 2048;
-    if (cached[dev] == 0) {
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quant_rows_kernel<DT, RL>, 256, 0) !=
                 hipSuccess ||
@@ -341,9 +345,10 @@ static int64_t rows_resident_blocks() {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
             cus <= 0)
             cus = 256;
-        cached[dev] = per_cu * cus;
+        v = per_cu * cus;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 static DivMagic make_div_magic(uint32_t d) {
