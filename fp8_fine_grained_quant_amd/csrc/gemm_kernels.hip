@@ -14,9 +14,8 @@
 // partial-sum register set and independent VALU FMAs fold the previous
 // partial into the FP32 accumulator while the next MFMA runs.
 //
-// Two schedules share the building blocks below: the BLOCK128 GEMMs (Fprop,
-// Dgrad, the grouped MoE GEMM) run the ping-pong kernel gemm_pp_kernel, the
-// ROW128 GEMM (Wgrad) the single-phase gemm_kernel.
+// All of them -- BLOCK128 (Fprop, Dgrad, the grouped MoE GEMM) and ROW128
+// (Wgrad) -- run the ping-pong kernel gemm_pp_kernel.
 //
 // Design (one workgroup = one 256x256 output tile, 8 waves, 2 per SIMD):
 //  * K step 128 = exactly one scale block, so each K step is one
@@ -280,221 +279,8 @@ __device__ __forceinline__ void store_out(const GemmParams& p, int64_t m, int64_
     }
 }
 
-template <int SCALE_MODE, int OUT, bool GROUPED, bool POW2>
-__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
-    // [stage][0..255]: sa of the tile's rows; [stage][256..511]: ROW128: sb
-    // of the tile's columns; BLOCK128: the two 128x128-block weight scales of
-    // the tile's column halves, at [256] and [257] (each fetched by 32 lanes)
-    __shared__ __attribute__((aligned(16))) float smem_s[2][BM + BN];
-    __shared__ int32_t tile_start[GROUPED ? (kMaxGroups + 1) : 1];
-    __shared__ int32_t wave_tot[kThreads / 64];
-
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps it in SGPRs
-    const int lane = tid & 63;
-    const int wm = wave & 3;   // wave row (64 rows each)
-    const int wn = wave >> 2;  // wave column (128 columns each)
-
-    const int64_t N = p.N;
-    const uint8_t* bptr = p.b;
-    const float* sbptr = p.sb;
-    int64_t m0, m_end, n0;
-
-    if (!locate_tile<GROUPED>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
-        return;  // whole workgroup: uniform exit (grouped GEMM, surplus workgroup)
-
-    const int nkb = (int)(p.K / BK);
-    const int64_t nb_last = (N + 127) / 128 - 1;
-
-    // Per-lane copy sources, as 32-bit offsets from a wave-uniform base.
-    // Rows past the tile's end are clamped (their results are never stored).
-    // Offsets stay below 2^32: a tile spans 256 rows of at most 2^24 bytes
-    // each (the host rejects larger leading dimensions).
-    m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)m0) |
-         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)m0 >> 32)) << 32);
-    LoadCtx lc;
-    {
-        // copy instruction qd of wave w fills rows 8*(4w+qd) .. +7 of a slab:
-        // lane l carries row +l/8 and stores 16-byte slot l%8, which holds
-        // logical chunk swz(row, l%8)
-        lc.a_base = uniform_ptr(p.a + m0 * p.lda);
-        lc.b_base = uniform_ptr(bptr + n0 * p.ldb);
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const int row = (wave * 4 + qd) * 8 + (lane >> 3);
-            const uint32_t kbyte = (uint32_t)(swz(row, lane & 7) * 16);
-            lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + kbyte;
-            lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
-        }
-        if (SCALE_MODE == kScaleRow128 && wave >= 4) {
-            lc.s_base = uniform_ptr(sbptr + n0);
-            lc.s_off = (uint32_t)(min(n0 + (wave - 4) * 64 + lane, N - 1) - n0) * 4u;
-            lc.s_kstride = p.sbs0;
-        } else if (wave >= 4) {
-            // BLOCK128: lane l fetches the weight block scale of wave column
-            // l&1 (block n0/128 + (l&1)); smem_s[st][BM + wn] is then read
-            // by wave column wn.
-            lc.s_base = uniform_ptr(sbptr);
-            lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
-            lc.s_kstride = p.sbs1;
-        } else {
-            lc.s_base = uniform_ptr(p.sa + m0);
-            lc.s_off = (uint32_t)(min(m0 + (wave & 3) * 64 + lane, m_end - 1) - m0) * 4u;
-            lc.s_kstride = p.ldsa;
-        }
-    }
-    const int s_half = wave >= 4 ? BM : 0;  // which half of smem_s this wave fills
-
-    v4f acc[4][8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
-
-    // Software pipeline over K steps, two LDS stages.  Step kb runs the
-    // MFMAs of column blocks 0..6, then (after its last LDS read of stage
-    // kb&1) meets the other waves at one barrier, after which stage kb&1 is
-    // free and stage (kb+1)&1 holds step kb+1.  The copy of step kb+2 into
-    // the freed stage and the fragment loads of step kb+1 are then issued
-    // while block 7's MFMAs and the last promotions of step kb run, so the
-    // matrix pipe does not drain at the barrier.
-    const int r16 = lane & 15;
-    const int kq = lane >> 4;
-    auto stage_a = [&](int st) { return smem_ab[st]; };
-    auto stage_b = [&](int st) { return smem_ab[st] + kSlabBytes; };
-    auto stage_s = [&](int st) { return &smem_s[st][s_half]; };
-    auto copy_step = [&](int kb, int st) {
-        const int kbc = kb < nkb ? kb : nkb - 1;   // past the end: harmless refill
-#pragma unroll
-        for (int q = 0; q < 9; ++q)
-            issue_copy(q, lc, (int64_t)kbc * BK, kbc, stage_a(st), stage_b(st), stage_s(st), wave);
-    };
-
-    v8i af[4], bf[3];
-    float sc[4];
-    uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of sa rows, of the block's sb
-    auto load_step_frags = [&](int st) {
-        const uint8_t* sa_ = stage_a(st);
-        const uint8_t* sb_ = stage_b(st);
-        bf[0] = frag32(sb_, wn * 8 + 0, lane);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
-        bf[1] = frag32(sb_, wn * 8 + 1, lane);
-        bf[2] = frag32(sb_, wn * 8 + 2, lane);
-        if constexpr (POW2) {
-            if (SCALE_MODE == kScaleBlock128) sbb = e8m0_of(smem_s[st][BM + wn]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[st][wm * kWaveM + i * 16 + r16]);
-        } else {
-            const float sbv = SCALE_MODE == kScaleBlock128 ? smem_s[st][BM + wn] : 1.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sc[i] = smem_s[st][wm * kWaveM + i * 16 + r16] * sbv;
-        }
-    };
-
-    copy_step(0, 0);
-    stage_barrier();
-    copy_step(1, 1);
-    load_step_frags(0);
-
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int cur = kb & 1;
-        const uint8_t* cb_ = stage_b(cur);
-        v4f part[2][4];
-        // POW2, ROW128: the E8M0 exponent of the B row (l & 15) of column block j
-        auto sb_e8m0 = [&](int j) -> uint32_t {
-            if (SCALE_MODE == kScaleBlock128) return sbb;
-            return e8m0_of(smem_s[cur][BM + wn * kWaveN + j * 16 + r16]);
-        };
-        if constexpr (POW2) {
-            const uint32_t s0 = sb_e8m0(0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][0] = mfma_f8_scaled(bf[0], af[i], acc[i][0], s0, sab[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) part[0][i] = mfma_f8(bf[0], af[i]);
-        }
-        // ROW128: the four column scales of block j for this lane
-        auto row_scales = [&](int j) {
-            if (SCALE_MODE != kScaleRow128) return make_float4(1.f, 1.f, 1.f, 1.f);
-            return *reinterpret_cast<const float4*>(&smem_s[cur][BM + wn * kWaveN + j * 16 + kq * 4]);
-        };
-        // B fragments run two column blocks ahead of their MFMAs.
-#pragma unroll
-        for (int j = 1; j <= 6; ++j) {
-            if (j + 2 <= 7) bf[(j + 2) % 3] = frag32(cb_, wn * 8 + j + 2, lane);
-            if constexpr (POW2) {
-                const uint32_t sj = sb_e8m0(j);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    acc[i][j] = mfma_f8_scaled(bf[j % 3], af[i], acc[i][j], sj, sab[i]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part[j & 1][i] = mfma_f8(bf[j % 3], af[i]);
-                const float4 sbq = row_scales(j - 1);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    promote<SCALE_MODE>(acc[i][j - 1], part[(j - 1) & 1][i], sc[i], sbq);
-            }
-            // issue order inside the block: MFMA, 4 promotion FMAs, with the
-            // two fragment reads of block j+2 slotted after the first two
-            // MFMAs -- the other wave of the SIMD fills the MFMA shadow
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-                if (q < 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
-            }
-            // one scheduling region per column block keeps the partial sums
-            // of at most two blocks alive
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        const float4 sbq6 = row_scales(6), sbq7 = row_scales(7);
-        const uint32_t s7 = POW2 ? sb_e8m0(7) : 0u;
-        // every LDS read of stage cur has been issued: release it, and make
-        // step kb+1 (copied into cur^1 during the previous step) visible
-        stage_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        v4f last[4];
-        if constexpr (POW2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i][7] = mfma_f8_scaled(bf[7 % 3], af[i], acc[i][7], s7, sab[i]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) last[i] = mfma_f8(bf[7 % 3], af[i]);
-        }
-        float sc_old[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sc_old[i] = sc[i];
-        copy_step(kb + 2, cur);
-        __builtin_amdgcn_sched_barrier(0);
-        load_step_frags(cur ^ 1);   // after the last step: unused, harmless reads
-        if constexpr (!POW2) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][6], part[0][i], sc_old[i], sbq6);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) promote<SCALE_MODE>(acc[i][7], last[i], sc_old[i], sbq7);
-        }
-    }
-    wait_vm_all();
-
-    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 block ----
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * kWaveM + i * 16 + r16;
-        if (m >= m_end) continue;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t n = n0 + wn * kWaveN + j * 16 + kq * 4;
-            if (n >= N) continue;
-            store_out<OUT>(p, m, n, N, acc[i][j]);
-        }
-    }
-}
-
 // ---------------------------------------------------------------------------
-// Ping-pong schedule for the dense BLOCK128 GEMM (Fprop, Dgrad).
+// Ping-pong schedule.
 //
 // The two waves that share a SIMD belong to different groups: waves 0-3
 // (group 0) own the tile's output columns 0-127, waves 4-7 (group 1) columns
@@ -503,8 +289,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 // -- 16 matrix instructions on register-resident fragments, with their
 // promotions -- and every slot ends at a workgroup barrier.  On each SIMD one
 // wave therefore feeds the matrix pipe while the other one is held up by
-// memory traffic; in the single-phase kernel both waves stall on their
-// copies at the same time.  A wave runs, per K step kb,
+// memory traffic (with one schedule for all waves, both would stall on their
+// copies at the same time).  A wave runs, per K step kb,
 //   MEM(kb,0)  A fragments, B fragments of column blocks 0-3, the scales;
 //              issues the copies of its own 32 B rows of step kb+1 (into
 //              stage kb+1, whose B rows its group finished reading two
@@ -524,8 +310,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 //     have landed (its 4 B copies of step kb+1 and 5 copies of step kb+2 may
 //     still fly) before group 0 reads step kb+1 in the next slot;
 //   group 1, after COMP(kb,1): vmcnt(5) -- its B rows of step kb+1 too.
-// Results are bitwise identical to the single-phase kernel: every
-// accumulator sees the same operations in the same order.
+// Every accumulator sees the same operations in the same order as in a
+// plain one-wave-per-tile schedule, so results do not depend on it.
 // ---------------------------------------------------------------------------
 
 // Slot boundaries.  The scheduling barriers keep instructions (the matrix
@@ -553,12 +339,44 @@ __device__ __forceinline__ void slot_barrier_vm9() {
 constexpr int kPromoteDist = 4;
 constexpr int kPartRing = kPromoteDist + 1;
 
-template <int OUT, bool POW2, bool GROUPED>
+// Column scales of the current compute half in ROW128 mode: for column block
+// jj, this lane's 4 FP32 column scales, or (POW2) the E8M0 exponent of the
+// block's B row r16.  Empty for BLOCK128.
+template <bool ROW>
+struct RowScales {
+    __device__ uint32_t e8m0(int, uint32_t block_e) const { return block_e; }
+    __device__ float4 col(int) const { return make_float4(1.f, 1.f, 1.f, 1.f); }
+};
+template <>
+struct RowScales<true> {
+    float4 q[4];
+    uint32_t e[4];
+    // s: the wave's 128 column scales in LDS; h: the compute half
+    template <bool POW2>
+    __device__ __forceinline__ void load(const float* s, int h, int r16, int kq) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int c = (4 * h + jj) * 16;
+            if constexpr (POW2) e[jj] = e8m0_of(s[c + r16]);
+            else q[jj] = *reinterpret_cast<const float4*>(&s[c + kq * 4]);
+        }
+    }
+    __device__ uint32_t e8m0(int jj, uint32_t) const { return e[jj]; }
+    __device__ float4 col(int jj) const { return q[jj]; }
+};
+
+// SM: B scale granularity, kScaleBlock128 (one per 128x128 weight block) or
+// kScaleRow128 (one per B row = output column, per K step: the Wgrad GEMM).
+template <int OUT, bool POW2, bool GROUPED, int SM>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
+    constexpr bool ROW = SM == kScaleRow128;
+    // VALU instructions of one promotion: FMAs, plus (ROW128) the products of
+    // the row scale with the four column scales
+    constexpr int kPromoteValu = ROW ? 8 : 4;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
-    // [stage][0..255]: sa of the tile's rows; [stage][256 + g]: the weight
-    // block scale of column half g (fetched by the 64 lanes, lane l holding
-    // block n0/128 + (l & 1))
+    // [stage][0..255]: sa of the tile's rows.  [stage][256 + c]: BLOCK128 --
+    // c = g, the weight block scale of column half g (lane l fetches block
+    // n0/128 + (l & 1)); ROW128 -- the scale of the tile's column c.
     __shared__ __attribute__((aligned(16))) float smem_s[2][BM + BN];
     __shared__ int32_t tile_start[GROUPED ? (kMaxGroups + 1) : 1];
     __shared__ int32_t wave_tot[kThreads / 64];
@@ -582,8 +400,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 
     m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)m0) |
          ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)m0 >> 32)) << 32);
-    // Copy sources as in the single-phase kernel: copy qd of wave w moves
-    // rows 8*(4w+qd) .. +7 of a slab (group 0: B rows 0-127, group 1:
+    // Copy sources: copy qd of wave w moves rows 8*(4w+qd) .. +7 of a slab (group 0: B rows 0-127, group 1:
     // 128-255); rows past the tile's end are clamped.
     LoadCtx lc;
     lc.a_base = uniform_ptr(p.a + m0 * p.lda);
@@ -596,9 +413,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
     }
     if (g == 1) {
-        lc.s_base = uniform_ptr(sbptr);
-        lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
-        lc.s_kstride = p.sbs1;
+        if constexpr (ROW) {
+            // the tile's 256 column scales: wave 4+w, lane l -> column 64w + l
+            lc.s_base = uniform_ptr(sbptr + n0);
+            lc.s_off = (uint32_t)(min(n0 + (wave & 3) * 64 + lane, N - 1) - n0) * 4u;
+            lc.s_kstride = p.sbs0;
+        } else {
+            lc.s_base = uniform_ptr(sbptr);
+            lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
+            lc.s_kstride = p.sbs1;
+        }
     } else {
         lc.s_base = uniform_ptr(p.sa + m0);
         lc.s_off = (uint32_t)(min(m0 + wm * 64 + lane, m_end - 1) - m0) * 4u;
@@ -626,6 +450,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     v8i af[4], bf[4];
     float sc[4];
     uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of the sa rows and of sb
+    // ROW128: the half's column scales (empty for BLOCK128)
+    RowScales<ROW> rs;
 
     // COMP(kb,h): the 16 blocks (i, 4h+jj).  FP32 scales: each partial sum is
     // promoted kPromoteDist instructions after it was issued.
@@ -634,7 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt)
                 acc[tt >> 2][4 * h + (tt & 3)] = mfma_f8_scaled(
-                    bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)], sbb, sab[tt >> 2]);
+                    bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)],
+                    rs.e8m0(tt & 3, sbb), sab[tt >> 2]);
         } else {
             v4f part[kPartRing];
 #pragma unroll
@@ -642,8 +469,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                 if (tt < 16) part[tt % kPartRing] = mfma_f8(bf[tt & 3], af[tt >> 2]);
                 if (tt >= kPromoteDist) {
                     const int u = tt - kPromoteDist;
-                    promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u % kPartRing], sc[u >> 2],
-                                            make_float4(1.f, 1.f, 1.f, 1.f));
+                    if constexpr (ROW)
+                        promote<kScaleRow128>(acc[u >> 2][4 * h + (u & 3)], part[u % kPartRing],
+                                              sc[u >> 2], rs.col(u & 3));
+                    else
+                        promote<kScaleBlock128>(acc[u >> 2][4 * h + (u & 3)], part[u % kPartRing],
+                                                sc[u >> 2], make_float4(1.f, 1.f, 1.f, 1.f));
                 }
             }
             // issue order pinned: kPromoteDist matrix instructions, then
@@ -655,9 +486,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
             for (int tt = kPromoteDist; tt < 16; ++tt) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x002, 4 * kPromoteDist, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu * kPromoteDist, 0);
         }
         // pins the half's accumulators here, so that none of the slot's
         // (memory-free) instructions is sunk past its closing barrier
@@ -678,6 +509,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     stage_barrier();
     if (g == 1) slot_barrier();      // group 1 starts one slot later
 
+    // The K loop starts on a 64-byte boundary.  Its placement relative to the
+    // instruction fetch lines is worth 3-4 %: the same instructions, shifted
+    // by an unrelated change elsewhere in the file, ran 915-923 us instead
+    // of 874-886 us on the Fprop GEMM.
+    asm volatile(".p2align 6");
     for (int kb = 0; kb < nkb; ++kb) {
         const int cur = kb & 1;
         {   // MEM(kb,0)
@@ -688,14 +524,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + j, lane);
             if constexpr (POW2) {
-                sbb = e8m0_of(smem_s[cur][BM + g]);
+                if constexpr (!ROW) sbb = e8m0_of(smem_s[cur][BM + g]);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur][wm * kWaveM + i * 16 + r16]);
+            } else if constexpr (ROW) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16];
             } else {
                 const float sbv = smem_s[cur][BM + g];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16] * sbv;
             }
+            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWaveN], 0, r16, kq);
             copies(4, 8, kb + 1, cur ^ 1);
         }
         slot_barrier();
@@ -705,6 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
             const uint8_t* sb_ = stage_b(cur);
 #pragma unroll
             for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + 4 + j, lane);
+            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWaveN], 1, r16, kq);
             copies(0, 4, kb + 2, cur);
             copies(8, 9, kb + 2, cur);
         }
@@ -736,21 +577,21 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
     if (scale_mode == kScaleBlock128) {
         // dense Fprop / Dgrad: ping-pong schedule
         if (out_dtype == kBF16) {
-            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true, false>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false, false>), grid, block, 0, stream, p);
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true, false, kScaleBlock128>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false, false, kScaleBlock128>), grid, block, 0, stream, p);
         } else {
-            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true, false>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false, false>), grid, block, 0, stream, p);
+            if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true, false, kScaleBlock128>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false, false, kScaleBlock128>), grid, block, 0, stream, p);
         }
         return hipGetLastError();
     }
-    // ROW128 (Wgrad): single-phase kernel
+    // ROW128 (Wgrad): ping-pong with per-column B scales
     if (out_dtype == kBF16) {
-        if (pow2) hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kBF16, false, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kBF16, false, false>), grid, block, 0, stream, p);
+        if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true, false, kScaleRow128>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false, false, kScaleRow128>), grid, block, 0, stream, p);
     } else {
-        if (pow2) hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kF32, false, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_kernel<kScaleRow128, kF32, false, false>), grid, block, 0, stream, p);
+        if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true, false, kScaleRow128>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false, false, kScaleRow128>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }
@@ -760,7 +601,7 @@ hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, bool pow2, hi
     const int64_t tiles = ((p.M + BM - 1) / BM + p.num_groups) * ((p.N + BN - 1) / BN);
     dim3 grid((unsigned)tiles), block(kThreads);
 #define FP8Q_GGEMM(OD, P2) \
-    hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, true>), grid, block, 0, stream, p)
+    hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, true, kScaleBlock128>), grid, block, 0, stream, p)
     if (out_dtype == kBF16) {
         if (pow2) FP8Q_GGEMM(kBF16, true);
         else FP8Q_GGEMM(kBF16, false);
