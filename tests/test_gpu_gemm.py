@@ -50,7 +50,7 @@ def test_gemm_tiny_config_bf16(fq, oracle):
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 300, 256), (300, 200, 384), (256, 256, 128),
                                    (257, 513, 256), (512, 768, 1024), (33, 1000, 640),
-                                   (1000, 40, 512)])
+                                   (1000, 40, 512), (127, 129, 128), (129, 127, 384)])
 def test_gemm_shapes_and_tails(fq, oracle, M, N, K, out):
     rng = np.random.default_rng(M * 7 + N * 13 + K)
     a = _rand_scaled(rng, (M, K))

@@ -29,7 +29,8 @@ def _offsets(counts):
 @pytest.mark.parametrize("counts,N,K", [([0, 300, 1, 0, 257, 128], 384, 256),
                                         ([5], 256, 128),
                                         ([0, 0, 513], 200, 384),
-                                        ([1] * 40, 256, 256)])
+                                        ([1] * 40, 256, 256),
+                                        ([127, 129, 0, 1], 129, 128)])
 def test_grouped_small_full(fq, oracle, counts, N, K, out):
     rng = np.random.default_rng(len(counts) * 100 + N + K)
     off = _offsets(counts)
