@@ -37,6 +37,8 @@
 //    tiles share A rows and B columns in that XCD's L2.
 //  * Tails in M and N: loads clamp the row index (never read out of bounds),
 //    stores are masked.
+#include <atomic>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -50,7 +52,6 @@ constexpr int BN = 256;
 constexpr int BK = 128;
 constexpr int kThreads = 512;
 constexpr int kWaveM = 64;
-constexpr int kWaveN = 128;
 constexpr int kSlabBytes = BM * BK;          // one operand, one stage
 constexpr int kStageBytes = 2 * kSlabBytes;  // A + B
 constexpr int kGroupM = 8;                   // tile rows per swizzle group
@@ -189,13 +190,13 @@ __device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const 
 // tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them, in (m-tile, n-tile)
 // order -- and a binary search; returns false (for the whole workgroup) past
 // the last tile.  bptr / sbptr are advanced to the group's weight and scales.
-template <bool GROUPED>
+template <bool GROUPED, int TBN = BN>
 __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_start,
                                             int32_t* wave_tot, int tid, int lane, int wave,
                                             int64_t& m0, int64_t& m_end, int64_t& n0,
                                             const uint8_t*& bptr, const float*& sbptr) {
     const int64_t N = p.N;
-    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles_n = (N + TBN - 1) / TBN;
     if (!GROUPED) {
         const int64_t tiles_m = (p.M + BM - 1) / BM;
         const int64_t T = tiles_m * tiles_n;
@@ -206,7 +207,7 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_s
         const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
         const int64_t rem = t - grp * kGroupM * tiles_n;
         m0 = (first_m + rem % gm) * BM;
-        n0 = (rem / gm) * BN;
+        n0 = (rem / gm) * TBN;
         m_end = p.M;
         return true;
     }
@@ -249,7 +250,7 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_s
     const int64_t tn = local_t - tm * tiles_n;
     m0 = p.offsets[g] + tm * BM;
     m_end = p.offsets[g + 1];
-    n0 = tn * BN;
+    n0 = tn * TBN;
     bptr += (int64_t)g * N * p.ldb;
     sbptr += (int64_t)g * ((N + 127) / 128) * (p.K / 128);
     return true;
@@ -367,9 +368,16 @@ struct RowScales<true> {
 
 // SM: B scale granularity, kScaleBlock128 (one per 128x128 weight block) or
 // kScaleRow128 (one per B row = output column, per K step: the Wgrad GEMM).
-template <int OUT, bool POW2, bool GROUPED, int SM>
+template <int OUT, bool POW2, bool GROUPED, int SM, int TBN = BN>
 __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     constexpr bool ROW = SM == kScaleRow128;
+    // TBN: tile width, 256 or (ROW128 only) 224.  A wave owns kWN = TBN/2
+    // columns in NJ blocks of 16: 4 in the first compute half, NJ1 in the
+    // second.
+    static_assert(TBN == BN || (ROW && TBN == 224), "224-wide tiles need per-column scales");
+    constexpr int kWN = TBN / 2;
+    constexpr int NJ = kWN / 16;
+    constexpr int NJ1 = NJ - 4;
     // VALU instructions of one promotion: FMAs, plus (ROW128) the products of
     // the row scale with the four column scales
     constexpr int kPromoteValu = ROW ? 8 : 4;
@@ -393,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     const uint8_t* bptr = p.b;
     const float* sbptr = p.sb;
     int64_t m0, m_end, n0;
-    if (!locate_tile<GROUPED>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
+    if (!locate_tile<GROUPED, TBN>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
         return;  // whole workgroup: uniform exit (grouped GEMM, surplus workgroup)
     const int nkb = (int)(p.K / BK);
     const int64_t nb_last = (N + 127) / 128 - 1;
@@ -442,11 +450,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                            wave);
     };
 
-    v4f acc[4][8];
+    v4f acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     v8i af[4], bf[4];
     float sc[4];
     uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of the sa rows and of sb
@@ -456,18 +464,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     // COMP(kb,h): the 16 blocks (i, 4h+jj).  FP32 scales: each partial sum is
     // promoted kPromoteDist instructions after it was issued.
     auto comp = [&](int h) {
+        const int nj = h == 0 ? 4 : NJ1;    // column blocks of this half
         if constexpr (POW2) {
 #pragma unroll
             for (int tt = 0; tt < 16; ++tt)
-                acc[tt >> 2][4 * h + (tt & 3)] = mfma_f8_scaled(
-                    bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)],
-                    rs.e8m0(tt & 3, sbb), sab[tt >> 2]);
+                if ((tt & 3) < nj)
+                    acc[tt >> 2][4 * h + (tt & 3)] = mfma_f8_scaled(
+                        bf[tt & 3], af[tt >> 2], acc[tt >> 2][4 * h + (tt & 3)],
+                        rs.e8m0(tt & 3, sbb), sab[tt >> 2]);
         } else {
             v4f part[kPartRing];
 #pragma unroll
             for (int tt = 0; tt < 16 + kPromoteDist; ++tt) {
-                if (tt < 16) part[tt % kPartRing] = mfma_f8(bf[tt & 3], af[tt >> 2]);
-                if (tt >= kPromoteDist) {
+                if (tt < 16 && (tt & 3) < nj) part[tt % kPartRing] = mfma_f8(bf[tt & 3], af[tt >> 2]);
+                if (tt >= kPromoteDist && ((tt - kPromoteDist) & 3) < nj) {
                     const int u = tt - kPromoteDist;
                     if constexpr (ROW)
                         promote<kScaleRow128>(acc[u >> 2][4 * h + (u & 3)], part[u % kPartRing],
@@ -482,23 +492,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
             // partial (left to itself the scheduler packs the FMAs right
             // behind their own instruction, into hazard wait states)
 #pragma unroll
-            for (int tt = 0; tt < kPromoteDist; ++tt) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-#pragma unroll
-            for (int tt = kPromoteDist; tt < 16; ++tt) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu, 0);
+            for (int tt = 0; tt < 16 + kPromoteDist; ++tt) {
+                if (tt < 16 && (tt & 3) < nj) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (tt >= kPromoteDist && ((tt - kPromoteDist) & 3) < nj)
+                    __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x002, kPromoteValu * kPromoteDist, 0);
         }
         // pins the half's accumulators here, so that none of the slot's
         // (memory-free) instructions is sunk past its closing barrier
         const int j0 = 4 * h;
-        asm volatile("" : "+v"(acc[0][j0]), "+v"(acc[0][j0 + 1]), "+v"(acc[0][j0 + 2]),
-                          "+v"(acc[0][j0 + 3]), "+v"(acc[1][j0]), "+v"(acc[1][j0 + 1]),
-                          "+v"(acc[1][j0 + 2]), "+v"(acc[1][j0 + 3]), "+v"(acc[2][j0]),
-                          "+v"(acc[2][j0 + 1]), "+v"(acc[2][j0 + 2]), "+v"(acc[2][j0 + 3]),
-                          "+v"(acc[3][j0]), "+v"(acc[3][j0 + 1]), "+v"(acc[3][j0 + 2]),
-                          "+v"(acc[3][j0 + 3]));
+        if (nj == 4) {
+            asm volatile("" : "+v"(acc[0][j0]), "+v"(acc[0][j0 + 1]), "+v"(acc[0][j0 + 2]),
+                              "+v"(acc[0][j0 + 3]), "+v"(acc[1][j0]), "+v"(acc[1][j0 + 1]),
+                              "+v"(acc[1][j0 + 2]), "+v"(acc[1][j0 + 3]), "+v"(acc[2][j0]),
+                              "+v"(acc[2][j0 + 1]), "+v"(acc[2][j0 + 2]), "+v"(acc[2][j0 + 3]),
+                              "+v"(acc[3][j0]), "+v"(acc[3][j0 + 1]), "+v"(acc[3][j0 + 2]),
+                              "+v"(acc[3][j0 + 3]));
+        } else {
+            asm volatile("" : "+v"(acc[0][j0]), "+v"(acc[0][j0 + 1]), "+v"(acc[0][j0 + 2]),
+                              "+v"(acc[1][j0]), "+v"(acc[1][j0 + 1]), "+v"(acc[1][j0 + 2]),
+                              "+v"(acc[2][j0]), "+v"(acc[2][j0 + 1]), "+v"(acc[2][j0 + 2]),
+                              "+v"(acc[3][j0]), "+v"(acc[3][j0 + 1]), "+v"(acc[3][j0 + 2]));
+        }
     };
 
     // prologue: step 0 complete; step 1's A rows and scales (its B rows
@@ -522,7 +537,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + j, lane);
+            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * NJ + j, lane);
             if constexpr (POW2) {
                 if constexpr (!ROW) sbb = e8m0_of(smem_s[cur][BM + g]);
 #pragma unroll
@@ -535,7 +550,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16] * sbv;
             }
-            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWaveN], 0, r16, kq);
+            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWN], 0, r16, kq);
             copies(4, 8, kb + 1, cur ^ 1);
         }
         slot_barrier();
@@ -544,8 +559,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         {   // MEM(kb,1)
             const uint8_t* sb_ = stage_b(cur);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * 8 + 4 + j, lane);
-            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWaveN], 1, r16, kq);
+            for (int j = 0; j < 4; ++j)
+                if (j < NJ1) bf[j] = frag32(sb_, g * NJ + 4 + j, lane);
+            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWN], 1, r16, kq);
             copies(0, 4, kb + 2, cur);
             copies(8, 9, kb + 2, cur);
         }
@@ -562,12 +578,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         const int64_t m = m0 + wm * kWaveM + i * 16 + r16;
         if (m >= m_end) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t n = n0 + g * kWaveN + j * 16 + kq * 4;
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t n = n0 + g * kWN + j * 16 + kq * 4;
             if (n >= N) continue;
             store_out<OUT>(p, m, n, N, acc[i][j]);
         }
     }
+}
+
+// Compute units of the current device (cached per device; racing threads
+// store the same value).
+static int device_cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// Tile width of the ROW128 GEMM: the one with fewer column-passes,
+// ceil(tiles / CUs) * width (ties: 256).
+static int row_tile_n(int64_t M, int64_t N) {
+    const int64_t cus = device_cu_count();
+    const int64_t tm = (M + BM - 1) / BM;
+    auto cost = [&](int64_t w) { return ((tm * ((N + w - 1) / w) + cus - 1) / cus) * w; };
+    return cost(224) < cost(256) ? 224 : 256;
 }
 
 hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool pow2,
@@ -585,14 +625,24 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
         }
         return hipGetLastError();
     }
-    // ROW128 (Wgrad): ping-pong with per-column B scales
+    // ROW128 (Wgrad): per-column B scales; 224-wide tiles where they take
+    // fewer column-passes over the chip (ceil(tiles / CUs) * width), e.g.
+    // 2048 x 7168: 224 tiles of 256 on 256 CUs become 256 tiles of 224
+    const int tbn = row_tile_n(p.M, p.N);
+    dim3 g2((unsigned)(((p.M + BM - 1) / BM) * ((p.N + tbn - 1) / tbn)));
+#define FP8Q_ROW(OD, P2)                                                                                    \
+    do {                                                                                                    \
+        if (tbn == 224) hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, false, kScaleRow128, 224>), g2, block, 0, stream, p); \
+        else hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, false, kScaleRow128, 256>), g2, block, 0, stream, p);            \
+    } while (0)
     if (out_dtype == kBF16) {
-        if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kBF16, true, false, kScaleRow128>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_pp_kernel<kBF16, false, false, kScaleRow128>), grid, block, 0, stream, p);
+        if (pow2) FP8Q_ROW(kBF16, true);
+        else FP8Q_ROW(kBF16, false);
     } else {
-        if (pow2) hipLaunchKernelGGL((gemm_pp_kernel<kF32, true, false, kScaleRow128>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((gemm_pp_kernel<kF32, false, false, kScaleRow128>), grid, block, 0, stream, p);
+        if (pow2) FP8Q_ROW(kF32, true);
+        else FP8Q_ROW(kF32, false);
     }
+#undef FP8Q_ROW
     return hipGetLastError();
 }
 
