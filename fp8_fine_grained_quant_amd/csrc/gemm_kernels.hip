@@ -28,7 +28,7 @@
 //    bytes with an XOR chunk swizzle that keeps both the copies (8 lanes per
 //    row) coalesced and the fragment reads free of bank conflicts (see swz).
 //  * Wave tile 64(M) x 128(N): 4 x 8 blocks of 16x16, 128 FP32 accumulator
-//    VGPRs.  The MFMA is issued with the B slab as its first operand, so a
+//    VGPRs (64 x 112 in the 224-wide tiles of the ROW128 GEMM).  The MFMA is issued with the B slab as its first operand, so a
 //    lane's four result registers are four CONSECUTIVE output columns of one
 //    row: the epilogue writes 16-byte (FP32) or 8-byte (BF16) runs, and the
 //    128x128-block weight scale is a wave-uniform scalar.
