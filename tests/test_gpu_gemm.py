@@ -174,3 +174,24 @@ def test_gemm_wgrad_large(fq, oracle):
     torch.cuda.synchronize()
     _sampled_check(fq, oracle, qa_o, sa_o, qb_o, sb_o, c, oracle.SCALE_ROW128, None, False, 4,
                    "wgrad 2048x7168x8192 f32")
+
+
+@pytest.mark.parametrize("N", [7168, 16384])
+def test_gemm_row128_tile_widths(fq, oracle, N):
+    """ROW128 GEMMs pick 256x224 or 256x256 tiles by the number of passes
+    over 256 compute units: M = 2048 (8 tile rows) with N = 7168 gives 224
+    tiles of 256 (one pass) or 256 tiles of 224 (one pass, narrower) -> 224;
+    N = 16384 gives 512 tiles of 256 (two passes) or 592 of 224 (three) ->
+    256.  Both widths against the oracle, on sampled outputs."""
+    rng = np.random.default_rng(N)
+    T, M = 256, 2048                        # reduction over T tokens
+    dy = _rand_scaled(rng, (T, M))
+    x = _rand_scaled(rng, (T, N))
+    qa_o, sa_o = oracle.quant_1x128(dy, transposed=True)
+    qb_o, sb_o = oracle.quant_1x128(x, transposed=True)
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy), transposed=True)
+    qb, sb = fq.fp8_quant_1x128(to_dev(x), transposed=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qb, sb, out_dtype=torch.float32, scale_mode=fq.SCALE_ROW128)
+    torch.cuda.synchronize()
+    _sampled_check(fq, oracle, qa_o, sa_o, qb_o, sb_o, c, oracle.SCALE_ROW128, None, False, 5,
+                   f"row128 2048x{N}x256")
