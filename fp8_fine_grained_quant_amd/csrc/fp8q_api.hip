@@ -140,8 +140,9 @@ int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, cons
     if (b_scale_mode == FP8Q_SCALE_ROW128 && sbs0 < N) return FP8Q_EINVAL;
     if (b_scale_mode == FP8Q_SCALE_BLOCK128 && ((N + 127) / 128) * sbs0 > (int64_t(1) << 29))
         return FP8Q_EUNSUPPORTED;  // 32-bit byte offsets into sb
-    // the tile grid is one workgroup per 256x256 output tile
-    if ((M + 255) / 256 * ((N + 255) / 256) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
+    // the tile grid is one workgroup per 256x256 output tile (256x224 for
+    // some ROW128 shapes: counted with the narrower width)
+    if ((M + 255) / 256 * ((N + 223) / 224) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
     fp8q::GemmParams p{};
     p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;
     p.b = b; p.ldb = ldb; p.sb = sb; p.sbs0 = sbs0; p.sbs1 = sbs1;
