@@ -125,4 +125,4 @@ def test_grouped_moe_config(fq, oracle):
                                                    qw_o, sw_o, off, mi, ni)
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, True, "moe grouped")
-    print(f"moe: {mi.size} sampled elements, max |err| / (1e-3 sum|ab|) = {r:.3g}")
+    print(f"moe: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
