@@ -256,26 +256,83 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_s
     return true;
 }
 
-// Stores a lane's four consecutive outputs C[m, n..n+3] (columns < N).
-template <int OUT>
-__device__ __forceinline__ void store_out(const GemmParams& p, int64_t m, int64_t n, int64_t N,
-                                          const v4f& v) {
-    if (OUT == kF32) {
-        float* cp = static_cast<float*>(p.c) + m * p.ldc + n;
-        if (n + 4 <= N) {
-            *reinterpret_cast<float4*>(cp) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-            for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = v[e];
+// Epilogue: the wave's 64 x kWN output block goes to C through a 4 KiB LDS
+// buffer of its own, in passes of 16 rows x 256 bytes.  A matrix instruction
+// leaves each lane 4 consecutive columns of one row, so a direct store writes
+// 16 rows x 32 bytes (BF16) per instruction: 16 partial-line requests.  After
+// the round trip through LDS a lane holds 16 consecutive bytes and a store
+// instruction covers 4 whole 256-byte row segments.  The 16-byte chunks of a
+// buffer row are XOR-swizzled with the row (chunk ^ (row & 15)), which keeps
+// both the fragment-order writes and the row-order reads free of bank
+// conflicts.  Rows past m_end and columns past N are not written.
+template <int OUT, int NJ>
+__device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)[4][NJ], uint8_t* buf,
+                                           int64_t m_base, int64_t m_end, int64_t n_base, int lane) {
+    const int64_t N = p.N;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int q = lane & 15;           // read side: 16-byte chunk of a buffer row
+    const int rq = lane >> 4;          // read side: row within a group of 4
+    // passes: BF16 -- one per row block i (NJ blocks of 16 columns = 2*NJ
+    // chunks); FP32 -- one per row block and half (up to 4 blocks = 16 chunks)
+    constexpr int kHalves = OUT == kF32 ? 2 : 1;
+#pragma unroll
+    for (int pass = 0; pass < 4 * kHalves; ++pass) {
+        const int i = pass / kHalves, h = pass % kHalves;
+        const int j0 = h * 4;
+        const int nj = OUT == kF32 ? (NJ - j0 < 4 ? NJ - j0 : 4) : NJ;
+        // this pass's row segment: columns n_base + ccol0 .. + 8*chunks - 1
+        const int ccol0 = OUT == kF32 ? j0 * 16 : 0;
+        const int nchunk = OUT == kF32 ? 4 * nj : 2 * nj;
+        asm volatile("" ::: "memory");   // the previous pass's reads stay before these writes
+#pragma unroll
+        for (int jj = 0; jj < 4 * 2; ++jj) {
+            if (jj >= nj) continue;
+            const v4f v = acc[i][j0 + jj];
+            if constexpr (OUT == kF32) {
+                const int ch = 4 * jj + kq;
+                *reinterpret_cast<float4*>(buf + r16 * 256 + ((ch ^ r16) << 4)) =
+                    make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                const int ch = 2 * jj + (kq >> 1);
+                *reinterpret_cast<uint2*>(buf + r16 * 256 + ((ch ^ r16) << 4) + (kq & 1) * 8) =
+                    make_uint2(float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16),
+                               float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16));
+            }
         }
-    } else {
-        uint16_t* cp = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
-        const uint32_t h0 = float_to_bf16_bits(v[0]), h1 = float_to_bf16_bits(v[1]);
-        const uint32_t h2 = float_to_bf16_bits(v[2]), h3 = float_to_bf16_bits(v[3]);
-        if (n + 4 <= N) {
-            *reinterpret_cast<uint2*>(cp) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-        } else {
-            const uint32_t h[4] = {h0, h1, h2, h3};
-            for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = (uint16_t)h[e];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int rl = 4 * t + rq;
+            const uint4 v = *reinterpret_cast<const uint4*>(buf + rl * 256 + ((q ^ rl) << 4));
+            const int64_t m = m_base + i * 16 + rl;
+            if (q >= nchunk || m >= m_end) continue;
+            if constexpr (OUT == kF32) {
+                const int64_t n = n_base + ccol0 + 4 * q;
+                if (n >= N) continue;
+                float* cp = static_cast<float*>(p.c) + m * p.ldc + n;
+                if (n + 4 <= N) {
+                    *reinterpret_cast<uint4*>(cp) = v;
+                } else {
+                    const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                                        __uint_as_float(v.w)};
+                    for (int e = 0; e < 4 && n + e < N; ++e) cp[e] = f[e];
+                }
+            } else {
+                const int64_t n = n_base + 8 * q;
+                if (n >= N) continue;
+                uint16_t* cp = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
+                if (n + 8 <= N) {
+                    if ((p.ldc & 7) == 0) {
+                        *reinterpret_cast<uint4*>(cp) = v;
+                    } else {   // ldc % 8 == 4: rows alternate between 16- and 8-byte alignment
+                        reinterpret_cast<uint2*>(cp)[0] = make_uint2(v.x, v.y);
+                        reinterpret_cast<uint2*>(cp)[1] = make_uint2(v.z, v.w);
+                    }
+                } else {
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                    for (int e = 0; e < 8 && n + e < N; ++e) cp[e] = (uint16_t)(w[e >> 1] >> ((e & 1) * 16));
+                }
+            }
         }
     }
 }
@@ -572,18 +629,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     if (g == 0) slot_barrier();      // group 0's idle last slot
     wait_vm_all();
 
-    // ---- epilogue: lane holds rows m, columns n..n+3 of each 16x16 block ----
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + wm * kWaveM + i * 16 + r16;
-        if (m >= m_end) continue;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int64_t n = n0 + g * kWN + j * 16 + kq * 4;
-            if (n >= N) continue;
-            store_out<OUT>(p, m, n, N, acc[i][j]);
-        }
-    }
+    // ---- epilogue ----
+    // every wave's copies have landed (the ones past the last step included):
+    // the stages are free; each wave takes its own 32 B rows of stage 1
+    __syncthreads();
+    store_tile<OUT, NJ>(p, acc, stage_b(1) + wave * 4096, m0 + wm * kWaveM, m_end, n0 + g * kWN, lane);
 }
 
 // Compute units of the current device (cached per device; racing threads
