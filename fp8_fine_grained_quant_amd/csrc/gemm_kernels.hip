@@ -37,6 +37,7 @@
 //    tiles share A rows and B columns in that XCD's L2.
 //  * Tails in M and N: loads clamp the row index (never read out of bounds),
 //    stores are masked.
+#include <algorithm>
 #include <atomic>
 
 #include "device_common.h"
@@ -164,7 +165,7 @@ __device__ __forceinline__ void issue_copy(int q, const LoadCtx& lc, int64_t kof
     else if (q < 8)
         dma16(lc.b_base + koff, lc.b_off[q - 4], lds_addr(st_b + (wave * 4 + q - 4) * 1024));
     else
-        dma4(lc.s_base + (int64_t)kb * lc.s_kstride, lc.s_off, lds_addr(st_s + (wave & 3) * 64));
+        dma4(uniform_ptr(lc.s_base + (int64_t)kb * lc.s_kstride), lc.s_off, lds_addr(st_s + (wave & 3) * 64));
 }
 
 // Promotion of one 16x16 block: acc += partial * scale (ROW128: the scale of
@@ -184,40 +185,69 @@ __device__ __forceinline__ void promote(v4f& a, const v4f& pp, float sci, const 
     }
 }
 
-// The output tile of this workgroup.  Dense: blockIdx -> (m0, n0) with each
-// XCD on a contiguous range of tiles, walked in groups of kGroupM tile rows.
-// Grouped: a tile table built in LDS -- group g owns tiles [tile_start[g],
-// tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them, in (m-tile, n-tile)
-// order -- and a binary search; returns false (for the whole workgroup) past
-// the last tile.  bptr / sbptr are advanced to the group's weight and scales.
-template <bool GROUPED, int TBN = BN>
-__device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_start,
-                                            int32_t* wave_tot, int tid, int lane, int wave,
-                                            int64_t& m0, int64_t& m_end, int64_t& n0,
-                                            const uint8_t*& bptr, const float*& sbptr) {
-    const int64_t N = p.N;
-    const int64_t tiles_n = (N + TBN - 1) / TBN;
-    if (!GROUPED) {
-        const int64_t tiles_m = (p.M + BM - 1) / BM;
-        const int64_t T = tiles_m * tiles_n;
-        int64_t t = blockIdx.x;
-        if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);  // contiguous range per XCD
-        const int64_t grp = t / (kGroupM * tiles_n);
-        const int64_t first_m = grp * kGroupM;
-        const int64_t gm = min(tiles_m - first_m, (int64_t)kGroupM);
-        const int64_t rem = t - grp * kGroupM * tiles_n;
-        m0 = (first_m + rem % gm) * BM;
-        n0 = (rem / gm) * TBN;
-        m_end = p.M;
-        return true;
-    }
+// Read-only memory seen through the constant address space: uniform
+// accesses become scalar loads (lgkmcnt), which leave the counted vmcnt
+// waits on the copies in flight undisturbed.
+typedef __attribute__((address_space(4))) const GemmParams* ConstParamsPtr;
+typedef __attribute__((address_space(4))) const int32_t* ConstI32Ptr;
+
+// The kernel's GemmParams, read from the kernel argument segment at the point
+// of use.  The persistent kernel needs most arguments again for every tile;
+// the empty asm hides where the pointer comes from, so the compiler reloads
+// them (scalar loads, cached) instead of pinning ~30 SGPRs for the whole
+// kernel.
+__device__ __forceinline__ GemmParams kparams() {
+    ConstParamsPtr q = (ConstParamsPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(q));
+    GemmParams r;
+    r.a = q->a; r.lda = q->lda; r.sa = q->sa; r.ldsa = q->ldsa;
+    r.b = q->b; r.ldb = q->ldb; r.sb = q->sb; r.sbs0 = q->sbs0; r.sbs1 = q->sbs1;
+    r.c = q->c; r.ldc = q->ldc; r.M = q->M; r.N = q->N; r.K = q->K;
+    r.offsets = q->offsets; r.num_groups = q->num_groups;
+    return r;
+}
+
+// An output tile: rows [m0, m_end) of C (m_end: the end of the tile's group,
+// or M), columns from n0, and the weight codes and block scales it uses.
+struct Tile {
+    int64_t m0, m_end, n0;
+    const uint8_t* b;
+    const float* sb;
+};
+
+// Dense tile t: each XCD gets a contiguous range of tiles (workgroups are
+// dealt to the XCDs round-robin), walked in groups of kGroupM tile rows so
+// that tiles running together share A rows and B columns in L2.
+// The tile count is below 2^31 (checked by the host), so the index
+// arithmetic runs in 32 bits.
+template <int TBN>
+__device__ __forceinline__ Tile dense_tile(const GemmParams& p, uint32_t t) {
+    const uint32_t tiles_n = (uint32_t)((p.N + TBN - 1) / TBN);
+    const uint32_t tiles_m = (uint32_t)((p.M + BM - 1) / BM);
+    const uint32_t T = tiles_m * tiles_n;
+    if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+    const uint32_t grp = t / (kGroupM * tiles_n);
+    const uint32_t first_m = grp * kGroupM;
+    const uint32_t gm = min(tiles_m - first_m, (uint32_t)kGroupM);
+    const uint32_t rem = t - grp * kGroupM * tiles_n;
+    return Tile{(int64_t)(first_m + rem % gm) * BM, p.M, (int64_t)(rem / gm) * TBN, p.b, p.sb};
+}
+
+// Grouped GEMM tile table in LDS: group g owns tiles [tile_start[g],
+// tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them in (m-tile, n-tile)
+// order.  Built once per workgroup from the device offsets (a block-wide
+// scan); returns the total tile count.
+template <int TBN>
+__device__ __forceinline__ int32_t grouped_table(const GemmParams& p, int32_t* tile_start,
+                                                 int32_t* wave_tot, int tid, int lane, int wave) {
     const int64_t G = p.num_groups;
+    const int32_t tiles_n = (int32_t)((p.N + TBN - 1) / TBN);
     const int per = (int)((G + kThreads - 1) / kThreads);
     const int g0 = tid * per;
     int32_t local = 0;
     for (int g = g0; g < g0 + per && g < G; ++g) {
         const int32_t rows = p.offsets[g + 1] - p.offsets[g];
-        local += (rows + BM - 1) / BM * (int32_t)tiles_n;
+        local += (rows + BM - 1) / BM * tiles_n;
     }
     int32_t incl = local;
 #pragma unroll
@@ -233,27 +263,37 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_s
     for (int g = g0; g < g0 + per && g < G; ++g) {
         tile_start[g] = run;
         const int32_t rows = p.offsets[g + 1] - p.offsets[g];
-        run += (rows + BM - 1) / BM * (int32_t)tiles_n;
+        run += (rows + BM - 1) / BM * tiles_n;
     }
     if (tid == kThreads - 1) tile_start[G] = run;
     __syncthreads();
-    const int32_t t = (int32_t)blockIdx.x;
-    if (t >= tile_start[G]) return false;
-    int lo = 0, hi = (int)G;         // tile_start[lo] <= t < tile_start[hi]
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (tile_start[mid] <= t) lo = mid; else hi = mid;
+    return __builtin_amdgcn_readfirstlane(tile_start[G]);
+}
+
+// Grouped tile t < tile_start[G]: its group is the last g with
+// tile_start[g] <= t.  A workgroup's tiles only increase, so the search runs
+// upward from gc (the previous tile's group), 64 table entries per step: the
+// entries <= t form a prefix of the window, counted with a ballot.
+template <int TBN>
+__device__ __forceinline__ Tile grouped_tile(const GemmParams& p, const int32_t* tile_start,
+                                             int32_t t, int& gc, int lane) {
+    const int G = (int)p.num_groups;
+    for (int it = 0; it <= G / 64 + 1; ++it) {
+        const int gi = gc + 1 + lane;
+        const bool le = gi <= G && tile_start[gi] <= t;
+        const int k = __popcll(__ballot(le));
+        gc = __builtin_amdgcn_readfirstlane(gc + k);
+        if (k < 64) break;
     }
-    const int g = lo;
-    const int32_t local_t = t - tile_start[g];
-    const int64_t tm = local_t / tiles_n;
-    const int64_t tn = local_t - tm * tiles_n;
-    m0 = p.offsets[g] + tm * BM;
-    m_end = p.offsets[g + 1];
-    n0 = tn * TBN;
-    bptr += (int64_t)g * N * p.ldb;
-    sbptr += (int64_t)g * ((N + 127) / 128) * (p.K / 128);
-    return true;
+    const int g = gc;
+    const int64_t N = p.N;
+    const int32_t tiles_n = (int32_t)((N + TBN - 1) / TBN);
+    const int32_t local_t = t - __builtin_amdgcn_readfirstlane(tile_start[g]);
+    const int32_t tm = local_t / tiles_n;
+    const int32_t tn = local_t - tm * tiles_n;
+    const ConstI32Ptr offs = (ConstI32Ptr)p.offsets;   // scalar loads (g is uniform)
+    return Tile{(int64_t)offs[g] + (int64_t)tm * BM, (int64_t)offs[g + 1], (int64_t)tn * TBN,
+                p.b + (int64_t)g * N * p.ldb, p.sb + (int64_t)g * ((N + 127) / 128) * (p.K / 128)};
 }
 
 // Epilogue: the wave's 64 x kWN output block goes to C through a 4 KiB LDS
@@ -268,6 +308,9 @@ __device__ __forceinline__ bool locate_tile(const GemmParams& p, int32_t* tile_s
 template <int OUT, int NJ>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)[4][NJ], uint8_t* buf,
                                            int64_t m_base, int64_t m_end, int64_t n_base, int lane) {
+    // (opaque: the per-lane address terms are computed here, per tile, not
+    // hoisted out of the tile loop and kept live through the K loop)
+    asm volatile("" : "+v"(lane));
     const int64_t N = p.N;
     const int r16 = lane & 15, kq = lane >> 4;
     const int q = lane & 15;           // read side: 16-byte chunk of a buffer row
@@ -455,51 +498,73 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     const int kq = lane >> 4;
 
     const int64_t N = p.N;
-    const uint8_t* bptr = p.b;
-    const float* sbptr = p.sb;
-    int64_t m0, m_end, n0;
-    if (!locate_tile<GROUPED, TBN>(p, tile_start, wave_tot, tid, lane, wave, m0, m_end, n0, bptr, sbptr))
-        return;  // whole workgroup: uniform exit (grouped GEMM, surplus workgroup)
     const int nkb = (int)(p.K / BK);
-    const int64_t nb_last = (N + 127) / 128 - 1;
 
-    m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)m0) |
-         ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)m0 >> 32)) << 32);
-    // Copy sources: copy qd of wave w moves rows 8*(4w+qd) .. +7 of a slab (group 0: B rows 0-127, group 1:
-    // 128-255); rows past the tile's end are clamped.
+    // Persistent: workgroup b runs tiles b, b + gridDim.x, ...
+    int64_t t = blockIdx.x;
+    int64_t total;
+    int gc = 0;   // grouped: group of the current tile
+    if constexpr (GROUPED) total = grouped_table<TBN>(p, tile_start, wave_tot, tid, lane, wave);
+    else total = ((p.M + BM - 1) / BM) * ((N + TBN - 1) / TBN);
+    if (t >= total) return;  // whole workgroup: uniform exit
+    auto locate = [&](int64_t tt) -> Tile {
+        if constexpr (GROUPED) return grouped_tile<TBN>(kparams(), tile_start, (int32_t)tt, gc, lane);
+        else return dense_tile<TBN>(kparams(), (uint32_t)tt);
+    };
+    Tile cur = locate(t);
+
+    // Copy sources: copy qd of wave w moves rows 8*(4w+qd) .. +7 of a slab
+    // (group 0: B rows 0-127, group 1: 128-255); rows past the tile's end
+    // are clamped.
     LoadCtx lc;
-    lc.a_base = uniform_ptr(p.a + m0 * p.lda);
-    lc.b_base = uniform_ptr(bptr + n0 * p.ldb);
+    auto set_lc = [&](const Tile& tl) {
+        const GemmParams p = kparams();
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));   // computed here, not hoisted (as in store_tile)
+        const int64_t N = p.N;
+        const int64_t nb_last = (N + 127) / 128 - 1;
+        const int64_t m0 = (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)tl.m0) |
+                           ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)tl.m0 >> 32)) << 32);
+        const int64_t n0 = tl.n0, m_end = tl.m_end;
+        lc.a_base = uniform_ptr(p.a + m0 * p.lda);
+        lc.b_base = uniform_ptr(tl.b + n0 * p.ldb);
 #pragma unroll
-    for (int qd = 0; qd < 4; ++qd) {
-        const int row = (wave * 4 + qd) * 8 + (lane >> 3);
-        const uint32_t kbyte = (uint32_t)(swz(row, lane & 7) * 16);
-        lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + kbyte;
-        lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
-    }
-    if (g == 1) {
-        if constexpr (ROW) {
-            // the tile's 256 column scales: wave 4+w, lane l -> column 64w + l
-            lc.s_base = uniform_ptr(sbptr + n0);
-            lc.s_off = (uint32_t)(min(n0 + (wave & 3) * 64 + lane, N - 1) - n0) * 4u;
-            lc.s_kstride = p.sbs0;
-        } else {
-            lc.s_base = uniform_ptr(sbptr);
-            lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
-            lc.s_kstride = p.sbs1;
+        for (int qd = 0; qd < 4; ++qd) {
+            const int row = (wave * 4 + qd) * 8 + (lane >> 3);
+            const uint32_t kbyte = (uint32_t)(swz(row, lane & 7) * 16);
+            lc.a_off[qd] = (uint32_t)((min(m0 + row, m_end - 1) - m0) * p.lda) + kbyte;
+            lc.b_off[qd] = (uint32_t)((min(n0 + row, N - 1) - n0) * p.ldb) + kbyte;
         }
-    } else {
-        lc.s_base = uniform_ptr(p.sa + m0);
-        lc.s_off = (uint32_t)(min(m0 + wm * 64 + lane, m_end - 1) - m0) * 4u;
-        lc.s_kstride = p.ldsa;
-    }
+        if (g == 1) {
+            if constexpr (ROW) {
+                // the tile's 256 column scales: wave 4+w, lane l -> column 64w + l
+                lc.s_base = uniform_ptr(tl.sb + n0);
+                lc.s_off = (uint32_t)(min(n0 + (wave & 3) * 64 + lane, N - 1) - n0) * 4u;
+                lc.s_kstride = p.sbs0;
+            } else {
+                lc.s_base = uniform_ptr(tl.sb);
+                lc.s_off = (uint32_t)(min((n0 >> 7) + (lane & 1), nb_last) * p.sbs0) * 4u;
+                lc.s_kstride = p.sbs1;
+            }
+        } else {
+            lc.s_base = uniform_ptr(p.sa + m0);
+            lc.s_off = (uint32_t)(min(m0 + wm * 64 + lane, m_end - 1) - m0) * 4u;
+            lc.s_kstride = p.ldsa;
+        }
+    };
+    set_lc(cur);
     const int s_half = g == 1 ? BM : 0;
     auto stage_a = [&](int st) { return smem_ab[st]; };
     auto stage_b = [&](int st) { return smem_ab[st] + kSlabBytes; };
     auto stage_s = [&](int st) { return &smem_s[st][s_half]; };
-    // copy instructions q0 .. q1-1 (0-3 A rows, 4-7 B rows, 8 scales) of step kb
+    // Copy instructions q0 .. q1-1 (0-3 A rows, 4-7 B rows, 8 scales) of
+    // step kb - kboff of the tile lc points at.  kboff is 0, or nkb once lc
+    // has moved on to the next tile; steps past the last one refill it
+    // (harmless: nothing reads them).
+    int kboff = 0;
     auto copies = [&](int q0, int q1, int kb, int st) {
-        const int kbc = kb < nkb ? kb : nkb - 1;   // past the end: harmless refill
+        int kbc = kb - kboff;
+        if (kbc >= nkb) kbc = nkb - 1;
 #pragma unroll
         for (int q = 0; q < 9; ++q)
             if (q >= q0 && q < q1)
@@ -508,10 +573,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     };
 
     v4f acc[4][NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
     v8i af[4], bf[4];
     float sc[4];
     uint32_t sab[4] = {}, sbb = 0;   // POW2: E8M0 exponents of the sa rows and of sb
@@ -573,67 +634,109 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         }
     };
 
-    // prologue: step 0 complete; step 1's A rows and scales (its B rows
-    // come with MEM(0,0))
+    // Stage of step kb of the current tile: (kb + sbase) & 1.  The first
+    // tile's prologue: step 0 complete; step 1's A rows and scales (its B
+    // rows come with MEM(0,0)).  A later tile's step 0 and step 1 A rows and
+    // scales are copied during the last two steps of the tile before it
+    // (when K spans at least two steps), so it starts without a prologue.
+    int sbase = 0;
     copies(0, 9, 0, 0);
     copies(0, 4, 1, 1);
     copies(8, 9, 1, 1);
     stage_barrier();
-    if (g == 1) slot_barrier();      // group 1 starts one slot later
+    for (;;) {
+        const int64_t t_next = t + gridDim.x;
+        const bool ahead = nkb >= 2 && t_next < total;   // next tile copied during this one
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = (v4f){0.f, 0.f, 0.f, 0.f};
+        kboff = 0;
+        if (g == 1) slot_barrier();      // group 1 starts one slot later
 
-    // The K loop starts on a 64-byte boundary.  Its placement relative to the
-    // instruction fetch lines is worth 3-4 %: the same instructions, shifted
-    // by an unrelated change elsewhere in the file, ran 915-923 us instead
-    // of 874-886 us on the Fprop GEMM.
-    asm volatile(".p2align 6");
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int cur = kb & 1;
-        {   // MEM(kb,0)
-            const uint8_t* sa_ = stage_a(cur);
-            const uint8_t* sb_ = stage_b(cur);
+        // The K loop starts on a 64-byte boundary.  Its placement relative to
+        // the instruction fetch lines is worth 3-4 %: the same instructions,
+        // shifted by an unrelated change elsewhere in the file, ran 915-923 us
+        // instead of 874-886 us on the Fprop GEMM.
+        asm volatile(".p2align 6");
+        for (int kb = 0; kb < nkb; ++kb) {
+            const int cur_st = (kb + sbase) & 1;
+            {   // MEM(kb,0)
+                const uint8_t* sa_ = stage_a(cur_st);
+                const uint8_t* sb_ = stage_b(cur_st);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
+                for (int i = 0; i < 4; ++i) af[i] = frag32(sa_, wm * 4 + i, lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * NJ + j, lane);
-            if constexpr (POW2) {
-                if constexpr (!ROW) sbb = e8m0_of(smem_s[cur][BM + g]);
+                for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * NJ + j, lane);
+                if constexpr (POW2) {
+                    if constexpr (!ROW) sbb = e8m0_of(smem_s[cur_st][BM + g]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur][wm * kWaveM + i * 16 + r16]);
-            } else if constexpr (ROW) {
+                    for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur_st][wm * kWaveM + i * 16 + r16]);
+                } else if constexpr (ROW) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16];
-            } else {
-                const float sbv = smem_s[cur][BM + g];
+                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_st][wm * kWaveM + i * 16 + r16];
+                } else {
+                    const float sbv = smem_s[cur_st][BM + g];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur][wm * kWaveM + i * 16 + r16] * sbv;
+                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_st][wm * kWaveM + i * 16 + r16] * sbv;
+                }
+                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_st][BM + g * kWN], 0, r16, kq);
+                copies(4, 8, kb + 1, cur_st ^ 1);
             }
-            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWN], 0, r16, kq);
-            copies(4, 8, kb + 1, cur ^ 1);
-        }
-        slot_barrier();
-        comp(0);
-        slot_barrier();
-        {   // MEM(kb,1)
-            const uint8_t* sb_ = stage_b(cur);
+            slot_barrier();
+            comp(0);
+            slot_barrier();
+            {   // MEM(kb,1)
+                const uint8_t* sb_ = stage_b(cur_st);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                if (j < NJ1) bf[j] = frag32(sb_, g * NJ + 4 + j, lane);
-            if constexpr (ROW) rs.template load<POW2>(&smem_s[cur][BM + g * kWN], 1, r16, kq);
-            copies(0, 4, kb + 2, cur);
-            copies(8, 9, kb + 2, cur);
+                for (int j = 0; j < 4; ++j)
+                    if (j < NJ1) bf[j] = frag32(sb_, g * NJ + 4 + j, lane);
+                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_st][BM + g * kWN], 1, r16, kq);
+                if (ahead && kb == nkb - 2) {   // from here on, copies fetch the next tile
+                    // (opaque to the compiler, so that the next tile's copy
+                    // offsets are computed here and not kept live through
+                    // the whole loop)
+                    int64_t tn = t_next;
+                    asm volatile("" : "+s"(tn));
+                    set_lc(locate(tn));
+                    kboff = nkb;
+                }
+                copies(0, 4, kb + 2, cur_st);
+                copies(8, 9, kb + 2, cur_st);
+            }
+            if (g == 1) slot_barrier_vm9(); else slot_barrier();
+            comp(1);
+            slot_barrier_vm5();
         }
-        if (g == 1) slot_barrier_vm9(); else slot_barrier();
-        comp(1);
-        slot_barrier_vm5();
-    }
-    if (g == 0) slot_barrier();      // group 0's idle last slot
-    wait_vm_all();
+        if (g == 0) slot_barrier();      // group 0's idle last slot
+        wait_vm_all();
 
-    // ---- epilogue ----
-    // every wave's copies have landed (the ones past the last step included):
-    // the stages are free; each wave takes its own 32 B rows of stage 1
-    __syncthreads();
-    store_tile<OUT, NJ>(p, acc, stage_b(1) + wave * 4096, m0 + wm * kWaveM, m_end, n0 + g * kWN, lane);
+        // ---- epilogue ----
+        // Every wave's copies have landed (the next tile's steps 0 and 1, or
+        // refills past the last step) and are published.  Each wave stores
+        // its block through its own 32 B rows of the stage the last step
+        // used, which nothing is copied into before the next tile's MEM(0,0)
+        // (issued by the same wave, after its epilogue).
+        __syncthreads();
+        const int last_st = (nkb - 1 + sbase) & 1;
+        store_tile<OUT, NJ>(kparams(), acc, stage_b(last_st) + wave * 4096, cur.m0 + wm * kWaveM,
+                            cur.m_end, cur.n0 + g * kWN, lane);
+        if (t_next >= total) break;
+        t = t_next;
+        sbase = (sbase + nkb) & 1;
+        cur = locate(t);
+        if (!ahead) {
+            // K spans one step: the next tile's prologue, once every wave's
+            // epilogue has read its LDS buffer
+            set_lc(cur);
+            kboff = 0;
+            __syncthreads();
+            copies(0, 9, 0, sbase);
+            copies(0, 4, 1, sbase ^ 1);
+            copies(8, 9, 1, sbase ^ 1);
+            stage_barrier();
+        }
+    }
 }
 
 // Compute units of the current device (cached per device; racing threads
@@ -660,10 +763,16 @@ static int row_tile_n(int64_t M, int64_t N) {
     return cost(224) < cost(256) ? 224 : 256;
 }
 
+// Persistent grid: one workgroup per compute unit (a workgroup takes most of
+// a CU's LDS), or fewer when there are fewer tiles.
+static unsigned persistent_grid(int64_t tiles) {
+    return (unsigned)std::min<int64_t>(tiles, device_cu_count());
+}
+
 hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool pow2,
                        hipStream_t stream) {
     const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-    dim3 grid((unsigned)tiles), block(kThreads);
+    dim3 grid(persistent_grid(tiles)), block(kThreads);
     if (scale_mode == kScaleBlock128) {
         // dense Fprop / Dgrad: ping-pong schedule
         if (out_dtype == kBF16) {
@@ -679,7 +788,7 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
     // fewer column-passes over the chip (ceil(tiles / CUs) * width), e.g.
     // 2048 x 7168: 224 tiles of 256 on 256 CUs become 256 tiles of 224
     const int tbn = row_tile_n(p.M, p.N);
-    dim3 g2((unsigned)(((p.M + BM - 1) / BM) * ((p.N + tbn - 1) / tbn)));
+    dim3 g2(persistent_grid(((p.M + BM - 1) / BM) * ((p.N + tbn - 1) / tbn)));
 #define FP8Q_ROW(OD, P2)                                                                                    \
     do {                                                                                                    \
         if (tbn == 224) hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, false, kScaleRow128, 224>), g2, block, 0, stream, p); \
@@ -699,7 +808,7 @@ hipError_t launch_gemm(const GemmParams& p, int scale_mode, int out_dtype, bool 
 hipError_t launch_grouped_gemm(const GemmParams& p, int out_dtype, bool pow2, hipStream_t stream) {
     // upper bound on the tile count: sum_g ceil(rows_g/BM) <= M/BM + groups
     const int64_t tiles = ((p.M + BM - 1) / BM + p.num_groups) * ((p.N + BN - 1) / BN);
-    dim3 grid((unsigned)tiles), block(kThreads);
+    dim3 grid(persistent_grid(tiles)), block(kThreads);
 #define FP8Q_GGEMM(OD, P2) \
     hipLaunchKernelGGL((gemm_pp_kernel<OD, P2, true, kScaleBlock128>), grid, block, 0, stream, p)
     if (out_dtype == kBF16) {
