@@ -140,8 +140,8 @@ int gemm_impl(const uint8_t* a, int64_t lda, const float* sa, int64_t ldsa, cons
     if (b_scale_mode == FP8Q_SCALE_ROW128 && sbs0 < N) return FP8Q_EINVAL;
     if (b_scale_mode == FP8Q_SCALE_BLOCK128 && ((N + 127) / 128) * sbs0 > (int64_t(1) << 29))
         return FP8Q_EUNSUPPORTED;  // 32-bit byte offsets into sb
-    // the tile grid is one workgroup per 256x256 output tile (256x224 for
-    // some ROW128 shapes: counted with the narrower width)
+    // tiles of 256x256 (256x224 for some ROW128 shapes: counted with the
+    // narrower width) are numbered with 32-bit indices
     if ((M + 255) / 256 * ((N + 223) / 224) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
     fp8q::GemmParams p{};
     p.a = a; p.lda = lda; p.sa = sa; p.ldsa = ldsa;

@@ -234,9 +234,9 @@ __device__ __forceinline__ Tile dense_tile(const GemmParams& p, uint32_t t) {
 }
 
 // Grouped GEMM tile table in LDS: group g owns tiles [tile_start[g],
-// tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them in (m-tile, n-tile)
-// order.  Built once per workgroup from the device offsets (a block-wide
-// scan); returns the total tile count.
+// tile_start[g+1]), ceil(rows_g/BM) * tiles_n of them.  Built once per
+// workgroup from the device offsets (a block-wide scan); returns the total
+// tile count.
 template <int TBN>
 __device__ __forceinline__ int32_t grouped_table(const GemmParams& p, int32_t* tile_start,
                                                  int32_t* wave_tot, int tid, int lane, int wave) {
@@ -270,7 +270,12 @@ __device__ __forceinline__ int32_t grouped_table(const GemmParams& p, int32_t* t
     return __builtin_amdgcn_readfirstlane(tile_start[G]);
 }
 
-// Grouped tile t < tile_start[G]: its group is the last g with
+// Grouped tile t < tile_start[G].  As for dense tiles, each XCD gets a
+// contiguous range of the table (when the tile count and the grid are
+// multiples of 8, which keeps a workgroup's tiles increasing), and a group's
+// tiles are walked in groups of kGroupM tile rows: without this every XCD
+// took one tile column of every group and all eight read each A tile (3.5-6 %
+// slower on 262,144-row problems).  The tile's group is the last g with
 // tile_start[g] <= t.  A workgroup's tiles only increase, so the search runs
 // upward from gc (the previous tile's group), 64 table entries per step: the
 // entries <= t form a prefix of the window, counted with a ballot.
@@ -278,6 +283,8 @@ template <int TBN>
 __device__ __forceinline__ Tile grouped_tile(const GemmParams& p, const int32_t* tile_start,
                                              int32_t t, int& gc, int lane) {
     const int G = (int)p.num_groups;
+    const int32_t T = __builtin_amdgcn_readfirstlane(tile_start[G]);
+    if ((T & 7) == 0 && (gridDim.x & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
     for (int it = 0; it <= G / 64 + 1; ++it) {
         const int gi = gc + 1 + lane;
         const bool le = gi <= G && tile_start[gi] <= t;
@@ -288,9 +295,15 @@ __device__ __forceinline__ Tile grouped_tile(const GemmParams& p, const int32_t*
     const int g = gc;
     const int64_t N = p.N;
     const int32_t tiles_n = (int32_t)((N + TBN - 1) / TBN);
-    const int32_t local_t = t - __builtin_amdgcn_readfirstlane(tile_start[g]);
-    const int32_t tm = local_t / tiles_n;
-    const int32_t tn = local_t - tm * tiles_n;
+    const int32_t first_t = __builtin_amdgcn_readfirstlane(tile_start[g]);
+    const int32_t local_t = t - first_t;
+    const int32_t tiles_m = (__builtin_amdgcn_readfirstlane(tile_start[g + 1]) - first_t) / tiles_n;
+    const int32_t grp = local_t / (kGroupM * tiles_n);
+    const int32_t first_m = grp * kGroupM;
+    const int32_t gm = min(tiles_m - first_m, (int32_t)kGroupM);
+    const int32_t rem = local_t - grp * kGroupM * tiles_n;
+    const int32_t tm = first_m + rem % gm;
+    const int32_t tn = rem / gm;
     const ConstI32Ptr offs = (ConstI32Ptr)p.offsets;   // scalar loads (g is uniform)
     return Tile{(int64_t)offs[g] + (int64_t)tm * BM, (int64_t)offs[g + 1], (int64_t)tn * TBN,
                 p.b + (int64_t)g * N * p.ldb, p.sb + (int64_t)g * ((N + 127) / 128) * (p.K / 128)};
@@ -500,14 +513,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     const int64_t N = p.N;
     const int nkb = (int)(p.K / BK);
 
-    // Persistent: workgroup b runs tiles b, b + gridDim.x, ...
-    int64_t t = blockIdx.x;
-    int64_t total;
+    // Persistent: workgroup b runs tiles b, b + gridDim.x, ...  Tile counts
+    // are below 2^31 (checked by the host), so t + gridDim.x fits 32 bits.
+    uint32_t t = blockIdx.x;
+    uint32_t total;
     int gc = 0;   // grouped: group of the current tile
-    if constexpr (GROUPED) total = grouped_table<TBN>(p, tile_start, wave_tot, tid, lane, wave);
-    else total = ((p.M + BM - 1) / BM) * ((N + TBN - 1) / TBN);
+    if constexpr (GROUPED) total = (uint32_t)grouped_table<TBN>(p, tile_start, wave_tot, tid, lane, wave);
+    else total = (uint32_t)(((p.M + BM - 1) / BM) * ((N + TBN - 1) / TBN));
     if (t >= total) return;  // whole workgroup: uniform exit
-    auto locate = [&](int64_t tt) -> Tile {
+    auto locate = [&](uint32_t tt) -> Tile {
         if constexpr (GROUPED) return grouped_tile<TBN>(kparams(), tile_start, (int32_t)tt, gc, lane);
         else return dense_tile<TBN>(kparams(), (uint32_t)tt);
     };
@@ -645,7 +659,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     copies(8, 9, 1, 1);
     stage_barrier();
     for (;;) {
-        const int64_t t_next = t + gridDim.x;
+        const uint32_t t_next = t + gridDim.x;
         const bool ahead = nkb >= 2 && t_next < total;   // next tile copied during this one
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -696,7 +710,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                     // (opaque to the compiler, so that the next tile's copy
                     // offsets are computed here and not kept live through
                     // the whole loop)
-                    int64_t tn = t_next;
+                    uint32_t tn = t_next;
                     asm volatile("" : "+s"(tn));
                     set_lc(locate(tn));
                     kboff = nkb;
