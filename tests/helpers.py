@@ -56,6 +56,33 @@ def sample_elements(M: int, N: int, seed: int, rows: int = 16, cols: int = 16,
     return key // N, key % N
 
 
+def per_tile_elements(m_starts, m_ends, N: int, seed: int, per: int = 4, tile_m: int = 256,
+                      tile_n: int = 256):
+    """`per` seeded random elements inside every output tile: rows are cut
+    into tiles of tile_m from each start in m_starts up to the matching end
+    (one start/end pair per group; a dense GEMM is one group), columns into
+    tiles of tile_n."""
+    rng = np.random.default_rng(seed)
+    ms, ns = [], []
+    for m0, m1 in zip(m_starts, m_ends):
+        for r0 in range(int(m0), int(m1), tile_m):
+            r1 = min(int(m1), r0 + tile_m)
+            for c0 in range(0, N, tile_n):
+                c1 = min(N, c0 + tile_n)
+                ms.append(rng.integers(r0, r1, per))
+                ns.append(rng.integers(c0, c1, per))
+    if not ms:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    return np.concatenate(ms).astype(np.int64), np.concatenate(ns).astype(np.int64)
+
+
+def union_elements(N: int, *pairs):
+    """Union of (mi, ni) element lists, sorted row-major without repeats."""
+    key = np.unique(np.concatenate([np.asarray(m, np.int64) * N + np.asarray(n, np.int64)
+                                    for m, n in pairs]))
+    return key // N, key % N
+
+
 def check_gemm(c_gpu: np.ndarray, c_ref: np.ndarray, s_ref: np.ndarray, bf16_out: bool,
                what: str) -> float:
     """|gpu - C*| <= 1e-3 * S (+ one BF16 ulp of C* for BF16 output), all

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from fp8_fine_grained_quant_amd import synth
-from helpers import check_gemm, sample_elements, to_dev
+from helpers import check_gemm, per_tile_elements, sample_elements, to_dev, union_elements
 
 pytestmark = pytest.mark.gpu
 
@@ -195,3 +195,31 @@ def test_gemm_row128_tile_widths(fq, oracle, N):
     torch.cuda.synchronize()
     _sampled_check(fq, oracle, qa_o, sa_o, qb_o, sb_o, c, oracle.SCALE_ROW128, None, False, 5,
                    f"row128 2048x{N}x256")
+
+
+@pytest.mark.parametrize("K,out", [(128, "bf16"), (256, "bf16"), (384, "bf16"), (384, "f32")])
+def test_gemm_persistent_tile_loop(fq, oracle, K, out):
+    """The GEMM runs one workgroup per compute unit, each looping over
+    several 256x256 tiles; during a tile's last two K steps it already copies
+    the next tile's first two.  8192 x 8192 is 1024 tiles (four per
+    workgroup on 256 CUs).  K = 128: one step, so a plain prologue per tile;
+    256: the copies switch to the next tile in the first step; 384: an odd
+    step count, so the LDS stage of step 0 alternates from tile to tile.
+    Oracle on sampled outputs, among them 4 random elements of every tile."""
+    M = N = 8192
+    rng = np.random.default_rng(K + 17)
+    a = _rand_scaled(rng, (M, K))
+    w = _rand_scaled(rng, (N, K), 1.0) * np.float32(0.05)
+    qa_o, sa_o = oracle.quant_1x128(a)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    qa, sa = fq.fp8_quant_1x128(to_dev(a))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    c = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=dt)
+    torch.cuda.synchronize()
+    mi, ni = union_elements(N, sample_elements(M, N, K), per_tile_elements([0], [M], N, K))
+    c_ref, s_ref = oracle.gemm_exact_elems(qa_o, sa_o, qw_o, sw_o, mi, ni)
+    assert torch.isfinite(c.float()).all(), "non-finite output"
+    cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, out == "bf16", f"persistent 8192x8192x{K} {out}")
+    print(f"8192x8192x{K} {out}: {mi.size} sampled elements, max |err| / tol = {r:.3g}")

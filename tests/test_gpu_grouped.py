@@ -7,7 +7,8 @@ import pytest
 import torch
 
 from fp8_fine_grained_quant_amd import synth
-from helpers import assert_same_bytes, check_gemm, codes, scale_bits, to_dev
+from helpers import (assert_same_bytes, check_gemm, codes, per_tile_elements, scale_bits, to_dev,
+                     union_elements)
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +127,36 @@ def test_grouped_moe_config(fq, oracle):
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, True, "moe grouped")
     print(f"moe: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+
+
+@pytest.mark.parametrize("K", [128, 384])
+def test_grouped_persistent_tile_loop(fq, oracle, K):
+    """Twelve groups of uneven size, three of them empty, 15,618 rows x 2048
+    columns: 520 tiles, so workgroups (one per compute unit) run two or three
+    tiles each, moving from group to group, with the next tile's first
+    copies issued during the current one (K = 384, an odd step count) or a
+    plain prologue per tile (K = 128).  Oracle on 4 random elements of every
+    tile and on the first and last row of every group."""
+    counts = [2048, 0, 1999, 2300, 0, 1, 2048, 777, 4096, 0, 300, 2049]
+    N, G = 2048, len(counts)
+    off = _offsets(counts)
+    Mt = int(off[-1])
+    rng = np.random.default_rng(K + 3)
+    x = (rng.standard_normal((Mt, K)) * np.exp(rng.uniform(-3, 3, (Mt, 1)))).astype(np.float32)
+    w = (rng.standard_normal((G * N, K)) * 0.05).astype(np.float32)
+    qa_o, sa_o = oracle.quant_1x128(x)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    qa, sa = fq.fp8_quant_1x128(to_dev(x))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    c = fq.fp8_grouped_gemm(qa, sa, qw.view(G, N, K), sw.view(G, N // 128, K // 128),
+                            torch.from_numpy(off).cuda(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    firsts = [(np.full(N, off[g]), np.arange(N)) for g in range(G) if counts[g]]
+    lasts = [(np.full(N, off[g + 1] - 1), np.arange(N)) for g in range(G) if counts[g]]
+    mi, ni = union_elements(N, per_tile_elements(off[:-1], off[1:], N, K), *firsts, *lasts)
+    c_ref, s_ref = oracle.grouped_gemm_exact_elems(qa_o, sa_o, qw_o.reshape(G, N, K),
+                                                   sw_o.reshape(G, N // 128, K // 128), off, mi, ni)
+    assert torch.isfinite(c.float()).all(), "non-finite output"
+    cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, True, f"grouped persistent K={K}")
+    print(f"grouped {Mt} rows x {N} x {K}: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
