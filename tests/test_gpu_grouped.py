@@ -160,3 +160,40 @@ def test_grouped_persistent_tile_loop(fq, oracle, K):
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, True, f"grouped persistent K={K}")
     print(f"grouped {Mt} rows x {N} x {K}: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+
+
+def test_grouped_many_empty_groups(fq, oracle):
+    """4096 groups (the largest count the on-chip tile table holds), ten of
+    them non-empty and scattered among long runs of empty ones: the tile ->
+    group search steps over up to 64 empty table entries at a time.  263
+    tiles, so the workgroups that run a second tile jump from the first
+    groups to groups 3000, 4000 and 4095.  Oracle on 4 random elements of
+    every tile and on the first and last row of every non-empty group."""
+    G, N, K = 4096, 256, 128
+    counts = np.zeros(G, dtype=np.int64)
+    for g, n in [(0, 3), (63, 300), (64, 1), (65, 256), (1000, 513), (2047, 7), (2048, 129),
+                 (3000, 64000), (4000, 260), (4095, 2)]:
+        counts[g] = n
+    off = _offsets(counts)
+    Mt = int(off[-1])
+    rng = np.random.default_rng(4096)
+    x = (rng.standard_normal((Mt, K)) * np.exp(rng.uniform(-3, 3, (Mt, 1)))).astype(np.float32)
+    nz = np.flatnonzero(counts)
+    w = np.zeros((G, N, K), dtype=np.float32)
+    w[nz] = (rng.standard_normal((nz.size, N, K)) * 0.05).astype(np.float32)
+    qa_o, sa_o = oracle.quant_1x128(x)
+    qw_o, sw_o, _ = oracle.quant_128x128(w.reshape(G * N, K))
+    qa, sa = fq.fp8_quant_1x128(to_dev(x))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w.reshape(G * N, K)))
+    c = fq.fp8_grouped_gemm(qa, sa, qw.view(G, N, K), sw.view(G, N // 128, K // 128),
+                            torch.from_numpy(off).cuda(), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    firsts = [(np.full(N, off[g]), np.arange(N)) for g in nz]
+    lasts = [(np.full(N, off[g + 1] - 1), np.arange(N)) for g in nz]
+    mi, ni = union_elements(N, per_tile_elements(off[:-1], off[1:], N, 7), *firsts, *lasts)
+    c_ref, s_ref = oracle.grouped_gemm_exact_elems(qa_o, sa_o, qw_o.reshape(G, N, K),
+                                                   sw_o.reshape(G, N // 128, K // 128), off, mi, ni)
+    assert torch.isfinite(c).all(), "non-finite output"
+    cg = c[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, False, "4096 groups")
+    print(f"4096 groups, {Mt} rows, {mi.size} sampled elements: max |err| / tol = {r:.3g}")
