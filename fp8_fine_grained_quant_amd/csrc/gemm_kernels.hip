@@ -17,7 +17,8 @@
 // All of them -- BLOCK128 (Fprop, Dgrad, the grouped MoE GEMM) and ROW128
 // (Wgrad) -- run the ping-pong kernel gemm_pp_kernel.
 //
-// Design (one workgroup = one 256x256 output tile, 8 waves, 2 per SIMD):
+// Design (256x256 output tiles; a persistent workgroup of 8 waves, 2 per
+// SIMD, on each compute unit loops over its tiles):
 //  * K step 128 = exactly one scale block, so each K step is one
 //    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 output block (scale
 //    operands set to 1.0; the FP32 block scales are applied by the
@@ -28,10 +29,13 @@
 //    bytes with an XOR chunk swizzle that keeps both the copies (8 lanes per
 //    row) coalesced and the fragment reads free of bank conflicts (see swz).
 //  * Wave tile 64(M) x 128(N): 4 x 8 blocks of 16x16, 128 FP32 accumulator
-//    VGPRs (64 x 112 in the 224-wide tiles of the ROW128 GEMM).  The MFMA is issued with the B slab as its first operand, so a
-//    lane's four result registers are four CONSECUTIVE output columns of one
-//    row: the epilogue writes 16-byte (FP32) or 8-byte (BF16) runs, and the
-//    128x128-block weight scale is a wave-uniform scalar.
+//    VGPRs (64 x 112 in the 224-wide tiles of the ROW128 GEMM).  The MFMA is
+//    issued with the B slab as its first operand, so a lane's four result
+//    registers are four CONSECUTIVE output columns of one row and the
+//    128x128-block weight scale is a wave-uniform scalar.  The epilogue
+//    turns the block around through LDS and stores whole row segments.
+//  * A tile's last two K steps already copy the next tile's first two, so a
+//    workgroup moves from tile to tile without a prologue.
 //  * Workgroup -> tile mapping keeps each XCD on a contiguous range of tiles
 //    and walks them in groups of 8 tile rows so that concurrently running
 //    tiles share A rows and B columns in that XCD's L2.
