@@ -41,14 +41,18 @@ int quant_1x128_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int
     // The kernels use 16-byte loads and 8-byte stores wherever the pointers
     // and pitches allow it, and element accesses elsewhere.
     if (xs_c == 1 && (xs_r >= cols || rows == 1)) {
-        // row-contiguous input
+        // row-contiguous input; a launch covers whole 4-row bands of fewer
+        // than 2^31 groups
+        if ((cols + 127) / 128 > (int64_t(1) << 24)) return FP8Q_EUNSUPPORTED;
         const int64_t ldx = rows == 1 ? cols : xs_r;
         return launch_status(fp8q::launch_quant_rows(x, x_dtype, rows, cols, ldx, q, ldq, s,
                                                      lds, rule, stream));
     }
     if (xs_r == 1 && (xs_c >= rows || cols == 1)) {
         // Stored transposed: physical tensor [cols, rows] with row pitch xs_c;
-        // 128x1 groups along its rows, codes written transposed.
+        // 128x1 groups along its rows, codes written transposed.  One
+        // workgroup per 128x128 tile.
+        if ((rows + 127) / 128 * ((cols + 127) / 128) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
         const int64_t ldx = cols == 1 ? rows : xs_c;
         return launch_status(fp8q::launch_quant_tiles(x, x_dtype, fp8q::kTileCols, cols, rows,
                                                       ldx, nullptr, 0, q, ldq, s, lds, rule,
@@ -67,6 +71,8 @@ int quant_128x128_impl(const void* w, int w_dtype, int64_t rows, int64_t cols, i
     if (ldw < cols || ldq < cols) return FP8Q_EINVAL;
     if (q_t && ldqt < rows) return FP8Q_EINVAL;
     if (!aligned(w, w_dtype == FP8Q_BF16 ? 2 : 4) || !aligned(s, 4)) return FP8Q_EALIGN;
+    // one workgroup per 128x128 block
+    if ((rows + 127) / 128 * ((cols + 127) / 128) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
     return launch_status(fp8q::launch_quant_tiles(w, w_dtype, fp8q::kTileBlock, rows, cols, ldw, q,
                                                   ldq, q_t, ldqt, s, 0, rule, stream));
 }

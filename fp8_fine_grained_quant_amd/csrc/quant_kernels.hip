@@ -141,18 +141,22 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, DivMagic d) {
     return (uint32_t)(((uint64_t)__umulhi(n, d.m) + n) >> d.l);
 }
 
-// Groups are numbered row-major, gi = r * gpr + g (gpr groups per row, fewer
-// than 2^31 per launch), so a wave streams through consecutive addresses.
-// The grid is a few resident rounds of waves striding over the groups; a
-// wave takes 4 * kRowUnroll consecutive groups per pass (slice = lane / 16
-// picks one of 4 per step), issuing all of its loads before it consumes
-// any, and every wave gets the same share however the rows fall.
+// Groups are numbered in bands of 4 rows, gi = (band * gpr + g) * 4 + rsub
+// (gpr groups per row, fewer than 2^31 per launch), so the 4 slices of a
+// wave (slice = lane / 16) take group g of 4 consecutive rows: each reads a
+// 256-byte row run and their 4 scales S[g][r..r+3] go out as one 16-byte
+// run (row-major numbering wrote every scale to a line of its own).  The
+// grid is a few resident rounds of waves striding over the groups; a wave
+// takes kRowUnroll such steps per pass (groups g, g+1, ...), issuing all of
+// its loads before it consumes any, and every wave gets the same share
+// however the rows fall.  Rows past the last one in the final band are
+// skipped.
 template <int DT, int RULE>
 __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict__ x, int64_t cols,
                                                          int64_t ldx, uint8_t* __restrict__ q,
                                                          int64_t ldq, float* __restrict__ s,
                                                          int64_t lds, uint32_t total, uint32_t gpr,
-                                                         DivMagic dm, bool vin, bool vout) {
+                                                         DivMagic dm, bool vin, bool vout, uint32_t nrows) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int slice = lane >> 4;
@@ -165,17 +169,20 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
         bool vec[kRowUnroll];
 #pragma unroll
         for (int u = 0; u < kRowUnroll; ++u) {
+            // bands of 4 rows: gi = (band * gpr + g) * 4 + rsub
             const uint32_t gi = base + 4 * u + slice;
-            rr[u] = div_magic(gi, dm);
-            gg[u] = gi - rr[u] * gpr;
+            const uint32_t bg = gi >> 2;
+            const uint32_t band = div_magic(bg, dm);
+            gg[u] = bg - band * gpr;
+            rr[u] = band * 4 + (gi & 3);
             const int64_t c0 = (int64_t)gg[u] * 128 + sl * 8;
-            vec[u] = vin && gi < total && c0 + 8 <= cols;
+            vec[u] = vin && gi < total && rr[u] < nrows && c0 + 8 <= cols;
             if (vec[u]) issue8<DT>(static_cast<const char*>(x) + (size_t)rr[u] * (size_t)ldx * esz, c0, raw[u]);
         }
 #pragma unroll
         for (int u = 0; u < kRowUnroll; ++u) {
             const uint32_t gi = base + 4 * u + slice;
-            if (gi >= total) continue;
+            if (gi >= total || rr[u] >= nrows) continue;
             const int64_t c0 = (int64_t)gg[u] * 128 + sl * 8;
             float v[8];
             if (vec[u]) unpack8<DT>(raw[u], v);
@@ -369,15 +376,15 @@ static hipError_t launch_rows_t(const void* x, int64_t rows, int64_t cols, int64
     // four resident rounds of workgroups (measured best among 1, 2, 4, 8)
     const int64_t cap = 4 * rows_resident_blocks<DT, RL>();
     // rows per launch: fewer than 2^31 groups, so 32-bit group indices
-    const int64_t chunk = ((int64_t)1 << 31) / gpr - 1;
+    const int64_t chunk = (((int64_t)1 << 31) / gpr - 4) / 4 * 4;
     for (int64_t r0 = 0; r0 < rows; r0 += chunk) {
         const int64_t nr = rows - r0 < chunk ? rows - r0 : chunk;
-        const int64_t total = nr * gpr;
+        const int64_t total = (nr + 3) / 4 * 4 * gpr;   // bands of 4 rows
         int64_t blocks = (total + 16 * kRowUnroll - 1) / (16 * kRowUnroll);
         if (blocks > cap) blocks = cap;
         hipLaunchKernelGGL((quant_rows_kernel<DT, RL>), dim3((unsigned)blocks), dim3(256), 0, stream,
                            static_cast<const char*>(x) + r0 * ldx * esz, cols, ldx, q + r0 * ldq,
-                           ldq, s + r0, lds, (uint32_t)total, (uint32_t)gpr, dm, vin, vout);
+                           ldq, s + r0, lds, (uint32_t)total, (uint32_t)gpr, dm, vin, vout, (uint32_t)nr);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

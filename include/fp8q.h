@@ -96,6 +96,9 @@ enum {
  * Any pitch is accepted; the kernel uses 16-byte loads where x and its
  * pitch are 16-byte aligned and 8-byte code stores where q and ldq are
  * 8-byte aligned, element accesses otherwise (slower).
+ * Size limits (else FP8Q_EUNSUPPORTED): row-contiguous input at most 2^24
+ * groups per row (cols <= 2^31); transposed input fewer than 2^31 128x128
+ * tiles.
  */
 int fp8_quant_1x128(const void* x, int x_dtype, int64_t rows, int64_t cols,
                     int64_t xs_r, int64_t xs_c, uint8_t* q, int64_t ldq,
@@ -117,6 +120,7 @@ int fp8_quant_1x128(const void* x, int x_dtype, int64_t rows, int64_t cols,
  *         as s[j + i*ceil(cols/128)] by the GEMM's scale strides.
  * Alignment: w aligned to its element size, s to 4 bytes, else FP8Q_EALIGN;
  * pitches as for fp8_quant_1x128 (vector accesses where aligned).
+ * Size limit (else FP8Q_EUNSUPPORTED): fewer than 2^31 128x128 blocks.
  */
 int fp8_quant_128x128(const void* w, int w_dtype, int64_t rows, int64_t cols,
                       int64_t ldw, uint8_t* q, int64_t ldq, float* s,

@@ -76,6 +76,11 @@ def test_quant_1x128_validation(lib):
     assert q1(lib, xs_r=100, xs_c=1) == EINVAL                      # pitch < cols
     # transposed view: physical [cols, rows] with pitch xs_c
     assert q1(lib, xs_r=1, xs_c=2) == EINVAL                        # pitch < rows
+    # size limits, checked before any device access (the pointers are never used)
+    big = (1 << 24) * 128 + 1                                       # 2^24 + 1 groups per row
+    assert q1(lib, cols=big, xs_r=big, ldq=big) == EUNSUPPORTED
+    assert q1(lib, rows=1 << 23, cols=1 << 32, xs_r=1, xs_c=1 << 23, ldq=1 << 32,
+              lds=1 << 23) == EUNSUPPORTED                         # 2^31 tiles, transposed
 
 
 def q2(lib, w=A, dt=1, rows=256, cols=256, ldw=256, q=A, ldq=256, s=A, qt=None, ldqt=0):
@@ -91,6 +96,7 @@ def test_quant_128x128_validation(lib):
     assert q2(lib, qt=A, ldqt=100) == EINVAL
     assert q2(lib, w=MIS) == EALIGN and q2(lib, dt=0, w=A + 2) == EALIGN
     assert q2(lib, s=A + 1) == EALIGN
+    assert q2(lib, rows=1 << 23, cols=1 << 32, ldw=1 << 32, ldq=1 << 32) == EUNSUPPORTED  # 2^31 blocks
 
 
 def gemm(lib, a=A, lda=512, sa=A, ldsa=256, b=A, ldb=512, sb=A, mode=0, sbs0=4, sbs1=1, c=A,
