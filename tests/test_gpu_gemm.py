@@ -223,3 +223,53 @@ def test_gemm_persistent_tile_loop(fq, oracle, K, out):
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, out == "bf16", f"persistent 8192x8192x{K} {out}")
     print(f"8192x8192x{K} {out}: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("T", [128, 384])
+def test_gemm_persistent_row128(fq, oracle, T, pow2):
+    """The ROW128 (weight-gradient) kernel through the persistent tile loop:
+    2048 x 16384 is 512 tiles of 256x256 (two per workgroup), reduced over
+    T = 128 tokens (one K step: a prologue per tile) or 384 (odd step count),
+    with FP32 or power-of-two scales.  Oracle on sampled outputs, among them
+    4 random elements of every tile."""
+    M, N = 2048, 16384
+    rng = np.random.default_rng(T + 31 + pow2)
+    dy = _rand_scaled(rng, (T, M))
+    x = _rand_scaled(rng, (T, N))
+    rule = oracle.RULE_POW2 if pow2 else oracle.RULE_FP32
+    qa_o, sa_o = oracle.quant_1x128(dy, transposed=True, rule=rule)
+    qb_o, sb_o = oracle.quant_1x128(x, transposed=True, rule=rule)
+    qa, sa = fq.fp8_quant_1x128(to_dev(dy), transposed=True, pow2=pow2)
+    qb, sb = fq.fp8_quant_1x128(to_dev(x), transposed=True, pow2=pow2)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qb, sb, out_dtype=torch.float32, scale_mode=fq.SCALE_ROW128,
+                                pow2=pow2)
+    torch.cuda.synchronize()
+    mi, ni = union_elements(N, sample_elements(M, N, T), per_tile_elements([0], [M], N, T))
+    c_ref, s_ref = oracle.gemm_exact_elems(qa_o, sa_o, qb_o, sb_o, mi, ni, mode=oracle.SCALE_ROW128)
+    assert torch.isfinite(c).all(), "non-finite output"
+    cg = c[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, False, f"row128 persistent T={T} pow2={pow2}")
+    print(f"row128 2048x16384x{T} pow2={pow2}: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+
+
+def test_gemm_persistent_pow2(fq, oracle):
+    """Power-of-two scales through the persistent tile loop: 8192 x 8192 x 384
+    (1024 tiles, odd step count), every tile sampled."""
+    M = N = 8192
+    K = 384
+    rng = np.random.default_rng(77)
+    a = _rand_scaled(rng, (M, K))
+    w = _rand_scaled(rng, (N, K), 1.0) * np.float32(0.05)
+    qa_o, sa_o = oracle.quant_1x128(a, rule=oracle.RULE_POW2)
+    qw_o, sw_o, _ = oracle.quant_128x128(w, rule=oracle.RULE_POW2)
+    qa, sa = fq.fp8_quant_1x128(to_dev(a), pow2=True)
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w), pow2=True)
+    c = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16, pow2=True)
+    torch.cuda.synchronize()
+    mi, ni = union_elements(N, sample_elements(M, N, 77), per_tile_elements([0], [M], N, 77))
+    c_ref, s_ref = oracle.gemm_exact_elems(qa_o, sa_o, qw_o, sw_o, mi, ni)
+    assert torch.isfinite(c.float()).all(), "non-finite output"
+    cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
+    r = check_gemm(cg, c_ref, s_ref, True, "pow2 persistent 8192x8192x384")
+    print(f"pow2 8192x8192x384: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
