@@ -200,6 +200,7 @@ typedef __attribute__((address_space(4))) const int32_t* ConstI32Ptr;
 // the empty asm hides where the pointer comes from, so the compiler reloads
 // them (scalar loads, cached) instead of pinning ~30 SGPRs for the whole
 // kernel.
+static_assert(sizeof(GemmParams) == 16 * 8, "kparams() copies each of GemmParams' 16 fields");
 __device__ __forceinline__ GemmParams kparams() {
     ConstParamsPtr q = (ConstParamsPtr)__builtin_amdgcn_kernarg_segment_ptr();
     asm volatile("" : "+s"(q));
