@@ -116,6 +116,27 @@ def test_gemm_padding_untouched_and_repeatable(fq, oracle):
     check_gemm(c2.cpu().numpy(), c_ref, s_ref, False, "padded")
 
 
+def test_gemm_bf16_pitch_and_tail(fq, oracle):
+    """BF16 output with a row pitch of 268 elements (536 bytes: every other
+    row starts 8 but not 16 bytes aligned, so 16-byte chunks are stored as
+    two 8-byte halves) and N = 261 (the last chunk of a row holds 5 columns).
+    Values against the oracle; the pitch padding stays untouched."""
+    rng = np.random.default_rng(29)
+    M, N, K, ldc = 300, 261, 384, 268
+    a = _rand_scaled(rng, (M, K))
+    w = _rand_scaled(rng, (N, K), 1.0) * np.float32(0.05)
+    qa, sa = fq.fp8_quant_1x128(to_dev(a))
+    qw, sw, _ = fq.fp8_quant_128x128(to_dev(w))
+    cbuf = torch.full((M, ldc), float("nan"), dtype=torch.bfloat16, device="cuda")
+    c = fq.fp8_blockscaled_gemm(qa, sa, qw, sw, out_dtype=torch.bfloat16, c=cbuf[:, :N])
+    torch.cuda.synchronize()
+    assert torch.isnan(cbuf[:, N:].float()).all(), "ldc padding was written"
+    qa_o, sa_o = oracle.quant_1x128(a)
+    qw_o, sw_o, _ = oracle.quant_128x128(w)
+    c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qw_o, sw_o)
+    check_gemm(c.float().cpu().numpy(), c_ref, s_ref, True, "bf16 pitch 268")
+
+
 def test_gemm_zero_groups_and_extreme_scales(fq, oracle):
     """All-zero K blocks (scale +0) and activations spanning ~2^+-40 in one
     row: the promotion must not produce NaN/Inf and stays within tolerance."""
