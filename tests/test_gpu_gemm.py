@@ -297,3 +297,49 @@ def test_gemm_persistent_pow2(fq, oracle):
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, True, "pow2 persistent 8192x8192x384")
     print(f"pow2 8192x8192x384: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+
+
+def test_gemm_random_shapes(fq, oracle):
+    """40 seeded random cases: M, N in [1, 2600), K a multiple of 128 up to
+    1024, row pitch N rounded up to 4 plus 0-8 elements, BF16 or FP32 out,
+    BLOCK128 or ROW128 scales, FP32 or power-of-two scale rule, and rows
+    scaled over up to e^+-4.  All of C against the oracle, padding
+    untouched."""
+    rng = np.random.default_rng(2024)
+    for case in range(40):
+        row, pow2, bf16 = rng.random() < 0.3, rng.random() < 0.3, rng.random() < 0.5
+        K = 128 * int(rng.integers(1, 9))
+        while True:
+            M, N = int(rng.integers(1, 2600)), int(rng.integers(1, 2600))
+            if M * N * K <= 3e8:
+                break
+        ldc = (N + 3) // 4 * 4 + 4 * int(rng.integers(0, 3))
+        rule = oracle.RULE_POW2 if pow2 else oracle.RULE_FP32
+        spread = rng.uniform(0, 4)
+        if row:
+            dy = (rng.standard_normal((K, M)) * np.exp(rng.uniform(-spread, spread, (K, 1)))).astype(np.float32)
+            x = (rng.standard_normal((K, N)) * np.exp(rng.uniform(-spread, spread, (K, 1)))).astype(np.float32)
+            qa_o, sa_o = oracle.quant_1x128(dy, transposed=True, rule=rule)
+            qb_o, sb_o = oracle.quant_1x128(x, transposed=True, rule=rule)
+            c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qb_o, sb_o, mode=oracle.SCALE_ROW128)
+            qa, sa = fq.fp8_quant_1x128(to_dev(dy), transposed=True, pow2=pow2)
+            qb, sb = fq.fp8_quant_1x128(to_dev(x), transposed=True, pow2=pow2)
+            mode = fq.SCALE_ROW128
+        else:
+            a = (rng.standard_normal((M, K)) * np.exp(rng.uniform(-spread, spread, (M, 1)))).astype(np.float32)
+            w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+            qa_o, sa_o = oracle.quant_1x128(a, rule=rule)
+            qb_o, sb_o, _ = oracle.quant_128x128(w, rule=rule)
+            c_ref, s_ref = oracle.gemm_exact(qa_o, sa_o, qb_o, sb_o)
+            qa, sa = fq.fp8_quant_1x128(to_dev(a), pow2=pow2)
+            qb, sb, _ = fq.fp8_quant_128x128(to_dev(w), pow2=pow2)
+            mode = fq.SCALE_BLOCK128
+        dt = torch.bfloat16 if bf16 else torch.float32
+        cbuf = torch.full((M, ldc), float("nan"), dtype=dt, device="cuda")
+        c = fq.fp8_blockscaled_gemm(qa, sa, qb, sb, out_dtype=dt, c=cbuf[:, :N], scale_mode=mode,
+                                    pow2=pow2)
+        torch.cuda.synchronize()
+        what = (f"case {case}: {'ROW128' if row else 'BLOCK128'} {M}x{N}x{K} ldc {ldc} "
+                f"{'bf16' if bf16 else 'f32'} pow2={pow2}")
+        assert torch.isnan(cbuf[:, N:].float()).all(), f"{what}: ldc padding was written"
+        check_gemm(c.float().cpu().numpy(), c_ref, s_ref, bf16, what)
