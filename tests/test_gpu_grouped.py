@@ -197,3 +197,37 @@ def test_grouped_many_empty_groups(fq, oracle):
     cg = c[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, False, "4096 groups")
     print(f"4096 groups, {Mt} rows, {mi.size} sampled elements: max |err| / tol = {r:.3g}")
+
+
+def test_grouped_random(fq, oracle):
+    """20 seeded random grouped GEMMs: 1-39 groups of 0-699 rows (a fifth of
+    them forced empty), N a multiple of 128 up to 512, K up to 640, BF16 or
+    FP32 out, FP32 or power-of-two scale rule.  All of C against the
+    oracle."""
+    rng = np.random.default_rng(777)
+    for case in range(20):
+        G = int(rng.integers(1, 40))
+        N, K = int(rng.integers(1, 5)) * 128, 128 * int(rng.integers(1, 6))
+        counts = rng.integers(0, 700, G) * (rng.random(G) < 0.8)
+        off = _offsets(counts)
+        Mt = int(off[-1])
+        if Mt == 0:
+            continue
+        pow2, bf16 = rng.random() < 0.3, rng.random() < 0.5
+        rule = oracle.RULE_POW2 if pow2 else oracle.RULE_FP32
+        x = (rng.standard_normal((Mt, K)) * np.exp(rng.uniform(-3, 3, (Mt, 1)))).astype(np.float32)
+        w = (rng.standard_normal((G * N, K)) * 0.05).astype(np.float32)
+        qa_o, sa_o = oracle.quant_1x128(x, rule=rule)
+        qw_o, sw_o, _ = oracle.quant_128x128(w, rule=rule)
+        mi, ni = np.meshgrid(np.arange(Mt), np.arange(N), indexing="ij")
+        c_ref, s_ref = oracle.grouped_gemm_exact_elems(qa_o, sa_o, qw_o.reshape(G, N, K),
+                                                       sw_o.reshape(G, N // 128, K // 128), off,
+                                                       mi.ravel(), ni.ravel())
+        qa, sa = fq.fp8_quant_1x128(to_dev(x), pow2=pow2)
+        qw, sw, _ = fq.fp8_quant_128x128(to_dev(w), pow2=pow2)
+        dt = torch.bfloat16 if bf16 else torch.float32
+        c = fq.fp8_grouped_gemm(qa, sa, qw.view(G, N, K), sw.view(G, N // 128, K // 128),
+                                torch.from_numpy(off).cuda(), out_dtype=dt, pow2=pow2)
+        torch.cuda.synchronize()
+        check_gemm(c.float().cpu().numpy().ravel(), c_ref, s_ref, bf16,
+                   f"case {case}: {G} groups, {Mt} rows, N {N}, K {K}, pow2={pow2}")

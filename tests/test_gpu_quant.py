@@ -214,3 +214,34 @@ def test_scale_division_every_positive_amax(fq, oracle, part):
     # y's code must split between 0x7D (416) and 0x7E (448) across the range:
     # the case is sensitive to inv's rounding, not stuck on one side
     assert 0 < near_mid < hi - lo
+
+
+def test_quant_random_shapes(fq, oracle):
+    """60 seeded random cases, bit for bit against the oracle: shapes up to
+    1500 x 1500, BF16 or FP32 input, rows scaled over e^+-8 with 1 % exact
+    zeros, FP32 or power-of-two scale rule, and each of the three groupings
+    (1x128, 128x1 on the stored tensor, 128x128)."""
+    rng = np.random.default_rng(4242)
+    for case in range(60):
+        R, C = int(rng.integers(1, 1500)), int(rng.integers(1, 1500))
+        pow2 = rng.random() < 0.3
+        rule = oracle.RULE_POW2 if pow2 else oracle.RULE_FP32
+        x = (rng.standard_normal((R, C)) * np.exp(rng.uniform(-8, 8, (R, 1)))).astype(np.float32)
+        x[rng.random((R, C)) < 0.01] = 0.0
+        bf = rng.random() < 0.7
+        xd = to_dev(x).to(torch.bfloat16) if bf else to_dev(x)
+        xo = xd.float().cpu().numpy()           # the values the device quantizes (BF16 is exact in FP32)
+        kind = int(rng.integers(0, 3))
+        if kind == 0:
+            q, s = fq.fp8_quant_1x128(xd, pow2=pow2)
+            qo, so = oracle.quant_1x128(xo, rule=rule)
+        elif kind == 1:
+            q, s = fq.fp8_quant_1x128(xd, transposed=True, pow2=pow2)
+            qo, so = oracle.quant_1x128(xo, transposed=True, rule=rule)
+        else:
+            q, s, _ = fq.fp8_quant_128x128(xd, pow2=pow2)
+            qo, so, _ = oracle.quant_128x128(xo, rule=rule)
+        torch.cuda.synchronize()
+        what = f"case {case}: grouping {kind} {R}x{C} {'bf16' if bf else 'f32'} pow2={pow2}"
+        assert_same_bytes(codes(q), qo, what + " codes")
+        assert_same_bytes(scale_bits(s), np.ascontiguousarray(so).view(np.uint32), what + " scales")
