@@ -91,3 +91,32 @@ def test_dispatch_moe_config(fq, oracle):
     assert_same_bytes(qs, qg_o, "dispatched codes (sample)")
     assert_same_bytes(ss.view(np.uint32), np.ascontiguousarray(sg_o).view(np.uint32),
                       "dispatched scales (sample)")
+
+
+def test_dispatch_random(fq, oracle):
+    """30 seeded random dispatches, bit for bit: T tokens up to 600, widths
+    up to 3000 (ragged, and aligned or not to 16 bytes), up to 1500 output
+    rows drawn from the tokens with repeats, 2 % of them out of range (left
+    unwritten)."""
+    rng = np.random.default_rng(3131)
+    for case in range(30):
+        T, C, R = int(rng.integers(1, 600)), int(rng.integers(1, 3000)), int(rng.integers(1, 1500))
+        x = _tokens(rng, T, C)
+        index = rng.integers(0, T, R).astype(np.int32)
+        bad = rng.random(R) < 0.02
+        index[bad] = rng.choice(np.array([-1, T, 2 ** 31 - 1], dtype=np.int32), int(bad.sum()))
+        qt, st = fq.fp8_quant_1x128(to_dev(x))
+        G = (C + 127) // 128
+        qbuf = torch.full((R, C), 0xAB, dtype=torch.uint8, device="cuda")
+        sbuf = torch.full((G, R), float("nan"), dtype=torch.float32, device="cuda")
+        fq.fp8_dispatch_rows(qt, st, torch.from_numpy(index).cuda(), q=qbuf, s=sbuf)
+        torch.cuda.synchronize()
+        q, s = codes(qbuf), sbuf.cpu().numpy()
+        what = f"case {case}: T {T} C {C} R {R}"
+        assert (q[bad] == 0xAB).all() and np.isnan(s[:, bad]).all(), what + ": skipped rows written"
+        good = ~bad
+        if good.any():
+            qg_o, sg_o = oracle.quant_1x128(x[index[good]])
+            assert_same_bytes(q[good], qg_o, what + " codes")
+            assert_same_bytes(s[:, good].view(np.uint32), np.ascontiguousarray(sg_o).view(np.uint32),
+                              what + " scales")
