@@ -415,9 +415,14 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)
 //              stage kb+1, whose B rows its group finished reading two
 //              slots earlier)
 //   COMP(kb,0) column blocks 0-3
-//   MEM(kb,1)  B fragments of column blocks 4-7; issues the copies of its
-//              32 A rows and its scale copy of step kb+2 (into stage kb,
-//              whose A rows and scales both groups have read by then)
+//   MEM(kb,1)  B fragments of column blocks 4-7 (ROW128: and the column
+//              scales of that half); issues the copies of its 32 A rows and
+//              its scale copy of step kb+2 (A rows into stage kb, which both
+//              groups have read by then; scales into the scale stage of
+//              step kb -- BLOCK128 -- whose scales are read only in
+//              MEM(kb,0), or -- ROW128, three scale stages -- of step kb-1,
+//              because group 1 reads step kb's column scales in this same
+//              slot while waves 6 and 7 issue the copy)
 //   COMP(kb,1) column blocks 4-7
 // with group 1 one slot behind group 0.  Every copy is issued at least four
 // slots before its first reader; each wave waits for its own copies with a
@@ -507,7 +512,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     // [stage][0..255]: sa of the tile's rows.  [stage][256 + c]: BLOCK128 --
     // c = g, the weight block scale of column half g (lane l fetches block
     // n0/128 + (l & 1)); ROW128 -- the scale of the tile's column c.
-    __shared__ __attribute__((aligned(16))) float smem_s[2][BM + BN];
+    // Scale stages: two (with the A/B stages) for BLOCK128; three for
+    // ROW128, where step kb+2's column scales are copied in the slot in which
+    // group 1 still reads step kb's (MEM(kb,1)).
+    constexpr int kSStages = ROW ? 3 : 2;
+    __shared__ __attribute__((aligned(16))) float smem_s[kSStages][BM + BN];
     __shared__ int32_t tile_start[GROUPED ? (kMaxGroups + 1) : 1];
     __shared__ int32_t wave_tot[kThreads / 64];
 
@@ -579,19 +588,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     const int s_half = g == 1 ? BM : 0;
     auto stage_a = [&](int st) { return smem_ab[st]; };
     auto stage_b = [&](int st) { return smem_ab[st] + kSlabBytes; };
-    auto stage_s = [&](int st) { return &smem_s[st][s_half]; };
+    auto stage_s = [&](int sst) { return &smem_s[sst][s_half]; };
     // Copy instructions q0 .. q1-1 (0-3 A rows, 4-7 B rows, 8 scales) of
-    // step kb - kboff of the tile lc points at.  kboff is 0, or nkb once lc
-    // has moved on to the next tile; steps past the last one refill it
-    // (harmless: nothing reads them).
+    // step kb - kboff of the tile lc points at, A and B rows into stage st,
+    // scales into scale stage sst.  kboff is 0, or nkb once lc has moved on
+    // to the next tile; steps past the last one refill it (harmless: nothing
+    // reads them).
     int kboff = 0;
-    auto copies = [&](int q0, int q1, int kb, int st) {
+    auto copies = [&](int q0, int q1, int kb, int st, int sst) {
         int kbc = kb - kboff;
         if (kbc >= nkb) kbc = nkb - 1;
 #pragma unroll
         for (int q = 0; q < 9; ++q)
             if (q >= q0 && q < q1)
-                issue_copy(q, lc, (int64_t)kbc * BK, kbc, stage_a(st), stage_b(st), stage_s(st),
+                issue_copy(q, lc, (int64_t)kbc * BK, kbc, stage_a(st), stage_b(st), stage_s(sst),
                            wave);
     };
 
@@ -662,10 +672,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     // rows come with MEM(0,0)).  A later tile's step 0 and step 1 A rows and
     // scales are copied during the last two steps of the tile before it
     // (when K spans at least two steps), so it starts without a prologue.
-    int sbase = 0;
-    copies(0, 9, 0, 0);
-    copies(0, 4, 1, 1);
-    copies(8, 9, 1, 1);
+    // ROW128: the scale stage of step kb is (kb + s3base) % 3.
+    int sbase = 0, s3base = 0;
+    auto sstage = [&](int kb, int st) { return ROW ? (kb + s3base) % 3 : st; };
+    copies(0, 9, 0, 0, sstage(0, 0));
+    copies(0, 4, 1, 1, sstage(1, 1));
+    copies(8, 9, 1, 1, sstage(1, 1));
     stage_barrier();
     for (;;) {
         const uint32_t t_next = t + gridDim.x;
@@ -684,6 +696,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         asm volatile(".p2align 6");
         for (int kb = 0; kb < nkb; ++kb) {
             const int cur_st = (kb + sbase) & 1;
+            const int cur_ss = sstage(kb, cur_st);   // scale stage of step kb
             {   // MEM(kb,0)
                 const uint8_t* sa_ = stage_a(cur_st);
                 const uint8_t* sb_ = stage_b(cur_st);
@@ -692,19 +705,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) bf[j] = frag32(sb_, g * NJ + j, lane);
                 if constexpr (POW2) {
-                    if constexpr (!ROW) sbb = e8m0_of(smem_s[cur_st][BM + g]);
+                    if constexpr (!ROW) sbb = e8m0_of(smem_s[cur_ss][BM + g]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur_st][wm * kWaveM + i * 16 + r16]);
+                    for (int i = 0; i < 4; ++i) sab[i] = e8m0_of(smem_s[cur_ss][wm * kWaveM + i * 16 + r16]);
                 } else if constexpr (ROW) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_st][wm * kWaveM + i * 16 + r16];
+                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_ss][wm * kWaveM + i * 16 + r16];
                 } else {
-                    const float sbv = smem_s[cur_st][BM + g];
+                    const float sbv = smem_s[cur_ss][BM + g];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_st][wm * kWaveM + i * 16 + r16] * sbv;
+                    for (int i = 0; i < 4; ++i) sc[i] = smem_s[cur_ss][wm * kWaveM + i * 16 + r16] * sbv;
                 }
-                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_st][BM + g * kWN], 0, r16, kq);
-                copies(4, 8, kb + 1, cur_st ^ 1);
+                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_ss][BM + g * kWN], 0, r16, kq);
+                copies(4, 8, kb + 1, cur_st ^ 1, 0);
             }
             slot_barrier();
             comp(0);
@@ -714,7 +727,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     if (j < NJ1) bf[j] = frag32(sb_, g * NJ + 4 + j, lane);
-                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_st][BM + g * kWN], 1, r16, kq);
+                if constexpr (ROW) rs.template load<POW2>(&smem_s[cur_ss][BM + g * kWN], 1, r16, kq);
                 if (ahead && kb == nkb - 2) {   // from here on, copies fetch the next tile
                     // (opaque to the compiler, so that the next tile's copy
                     // offsets are computed here and not kept live through
@@ -724,8 +737,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                     set_lc(locate(tn));
                     kboff = nkb;
                 }
-                copies(0, 4, kb + 2, cur_st);
-                copies(8, 9, kb + 2, cur_st);
+                copies(0, 4, kb + 2, cur_st, 0);
+                copies(8, 9, kb + 2, cur_st, sstage(kb + 2, cur_st));
             }
             if (g == 1) slot_barrier_vm9(); else slot_barrier();
             comp(1);
@@ -747,6 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
         if (t_next >= total) break;
         t = t_next;
         sbase = (sbase + nkb) & 1;
+        if constexpr (ROW) s3base = (s3base + nkb) % 3;
         cur = locate(t);
         if (!ahead) {
             // K spans one step: the next tile's prologue, once every wave's
@@ -754,9 +768,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
             set_lc(cur);
             kboff = 0;
             __syncthreads();
-            copies(0, 9, 0, sbase);
-            copies(0, 4, 1, sbase ^ 1);
-            copies(8, 9, 1, sbase ^ 1);
+            copies(0, 9, 0, sbase, sstage(0, sbase));
+            copies(0, 4, 1, sbase ^ 1, sstage(1, sbase ^ 1));
+            copies(8, 9, 1, sbase ^ 1, sstage(1, sbase ^ 1));
             stage_barrier();
         }
     }

@@ -174,6 +174,25 @@ def _out_code(dtype) -> int:
     raise TypeError("output dtype must be bfloat16 or float32")
 
 
+def _check_tensor(t: torch.Tensor, name: str, dtype, shape) -> None:
+    """t must have this dtype and shape and be unit-stride along its last
+    dimension (a size-1 last dimension may carry any stride)."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dim() >= 1 and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along its last dimension")
+
+
+def _check_out(c: torch.Tensor, M: int, N: int) -> None:
+    if c.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("c must be bfloat16 or float32")
+    _check_tensor(c, "c", c.dtype, (M, N))
+    if c.stride(1) != 1:
+        raise ValueError("c must be contiguous along dim 1")
+
+
 def _alloc_out(M: int, N: int, dtype, device) -> torch.Tensor:
     """Output [M, N] whose row pitch is a multiple of 4 elements (the GEMM
     stores 4 consecutive columns per lane); a view of a padded buffer when N
@@ -194,23 +213,30 @@ def fp8_blockscaled_gemm(a: torch.Tensor, sa: torch.Tensor, b: torch.Tensor, sb:
     >= N).  pow2=True calls fp8_blockscaled_gemm_pow2 (power-of-two scales
     applied by the matrix instruction)."""
     _require_cuda(a, sa, b, sb)
+    if a.dim() != 2 or b.dim() != 2:
+        raise ValueError("a and b must be 2-D")
     M, K = a.shape
     N = b.shape[0]
+    if a.dtype != torch.uint8 or b.dtype != torch.uint8:
+        raise TypeError("a and b must be uint8 E4M3 codes")
     if b.shape[1] != K or a.stride(1) != 1 or b.stride(1) != 1:
         raise ValueError("a, b must be [M,K] / [N,K] with K contiguous")
-    if sa.stride(1) != 1:
-        raise ValueError("sa must be contiguous along dim 1")
+    nkb = K // 128
+    _check_tensor(sa, "sa", torch.float32, (nkb, M))
     if scale_mode == SCALE_BLOCK128:
+        if sb.dtype != torch.float32 or tuple(sb.shape) != ((N + 127) // 128, nkb):
+            raise ValueError(f"BLOCK128 sb must be float32 [{(N + 127) // 128}, {nkb}] "
+                             f"(any strides), got {sb.dtype} {tuple(sb.shape)}")
         sbs0, sbs1 = sb.stride(0), sb.stride(1)
-    else:
-        if sb.stride(1) != 1:
-            raise ValueError("ROW128 sb must be contiguous along dim 1")
+    elif scale_mode == SCALE_ROW128:
+        _check_tensor(sb, "ROW128 sb", torch.float32, (nkb, N))
         sbs0, sbs1 = sb.stride(0), 0
+    else:
+        raise ValueError(f"unknown scale_mode {scale_mode}")
     if c is None:
         c = _alloc_out(M, N, out_dtype, a.device)
     _require_cuda(c)
-    if c.stride(1) != 1:
-        raise ValueError("c must be contiguous along dim 1")
+    _check_out(c, M, N)
     fn = _lib.fp8_blockscaled_gemm_pow2 if pow2 else _lib.fp8_blockscaled_gemm
     st = fn(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(b), b.stride(0), _ptr(sb),
             scale_mode, sbs0, sbs1, _ptr(c), _out_code(c.dtype), c.stride(0), M, N, K, _stream(a))
@@ -227,16 +253,24 @@ def fp8_grouped_gemm(a: torch.Tensor, sa: torch.Tensor, w: torch.Tensor, sw: tor
     per group), sw [G, ceil(N/128), K/128] contiguous; offsets int32 [G+1] on
     the device.  pow2=True calls fp8_grouped_gemm_pow2."""
     _require_cuda(a, sa, w, sw, offsets)
+    if a.dim() != 2 or w.dim() != 3:
+        raise ValueError("a must be 2-D and w 3-D")
     M, K = a.shape
     G, N, K2 = w.shape
+    if a.dtype != torch.uint8 or w.dtype != torch.uint8:
+        raise TypeError("a and w must be uint8 E4M3 codes")
     if K2 != K or a.stride(1) != 1 or w.stride(2) != 1 or w.stride(0) != N * w.stride(1):
         raise ValueError("a [M,K], w [G,N,K] with K contiguous and groups dense")
-    if not sw.is_contiguous() or tuple(sw.shape) != (G, (N + 127) // 128, K // 128):
-        raise ValueError("sw must be a contiguous [G, ceil(N/128), K/128] tensor")
-    if offsets.dtype != torch.int32 or offsets.numel() != G + 1:
-        raise ValueError("offsets must be int32 [G+1]")
+    _check_tensor(sa, "sa", torch.float32, (K // 128, M))
+    if (sw.dtype != torch.float32 or not sw.is_contiguous()
+            or tuple(sw.shape) != (G, (N + 127) // 128, K // 128)):
+        raise ValueError("sw must be a contiguous float32 [G, ceil(N/128), K/128] tensor")
+    if offsets.dtype != torch.int32 or offsets.numel() != G + 1 or not offsets.is_contiguous():
+        raise ValueError("offsets must be a contiguous int32 [G+1] tensor")
     if c is None:
         c = _alloc_out(M, N, out_dtype, a.device)
+    _require_cuda(c)
+    _check_out(c, M, N)
     fn = _lib.fp8_grouped_gemm_pow2 if pow2 else _lib.fp8_grouped_gemm
     st = fn(_ptr(a), a.stride(0), _ptr(sa), sa.stride(0), _ptr(w), w.stride(1), _ptr(sw),
             _ptr(offsets), G, M, _ptr(c), _out_code(c.dtype), c.stride(0), N, K, _stream(a))

@@ -10,8 +10,8 @@ Recipe (shared by every workload):
     ``standard_normal * std``;
   * outliers: ``round(frac * numel)`` positions chosen uniformly without
     replacement from the same generator, multiplied by ``factor`` -- the
-    activation outliers that make per-tensor scaling fragile (DeepSeek-V3
-    report, Section 3.3.1, on max-abs scaling and outliers);
+    activation outliers that make per-tensor scaling fragile ("Should
+    Fixing Deepseek Take 60 Steps?", max-abs scaling passage);
   * BF16 tensors are the float32 draw rounded to nearest-even BF16; they are
     returned as uint16 bit patterns (numpy has no bfloat16).
 MoE routing: expert popularity p_e proportional to rank_e^-1.1 (Zipf), ranks a
@@ -187,3 +187,48 @@ def moe_expert_weights(experts, n=2048, k=7168, out: np.ndarray | None = None,
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         list(ex.map(fill, range(len(experts))))
     return out
+
+
+# --- seeded output samples --------------------------------------------------------
+# Which output elements the large configurations are checked (and the CPU
+# baseline is timed) on: row and column indices only, no arithmetic.
+
+def output_sample(M: int, N: int, seed: int, rows: int = 64, cols: int = 64, rand: int = 4096,
+                  block: int = 128):
+    """`rows` full rows, `cols` full columns, `rand` random elements and every
+    element of the first and last block x block output tiles (which carry the
+    M and N tails), seeded; returns (mi, ni) sorted row-major, no repeats."""
+    rng = np.random.default_rng(seed)
+    ms, ns = [], []
+    for m in rng.choice(M, size=min(rows, M), replace=False):
+        ms.append(np.full(N, m))
+        ns.append(np.arange(N))
+    for n in rng.choice(N, size=min(cols, N), replace=False):
+        ms.append(np.arange(M))
+        ns.append(np.full(M, n))
+    ms.append(rng.integers(0, M, rand))
+    ns.append(rng.integers(0, N, rand))
+    for m0, n0 in ((0, 0), ((M - 1) // block * block, (N - 1) // block * block)):
+        mm, nn = np.meshgrid(np.arange(m0, min(M, m0 + block)), np.arange(n0, min(N, n0 + block)),
+                             indexing="ij")
+        ms.append(mm.ravel())
+        ns.append(nn.ravel())
+    mi = np.concatenate(ms).astype(np.int64)
+    ni = np.concatenate(ns).astype(np.int64)
+    key = np.unique(mi * N + ni)
+    return key // N, key % N
+
+
+def expert_rows(offsets: np.ndarray, seed: int, per: int = 8) -> np.ndarray:
+    """For every non-empty group of rows [offsets[e], offsets[e+1]): its first
+    and last row and `per` distinct random rows (all of them when fewer),
+    seeded; sorted, no repeats."""
+    rng = np.random.default_rng(seed)
+    rows = []
+    for e in range(len(offsets) - 1):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 <= r0:
+            continue
+        rows += [r0, r1 - 1]
+        rows += list(r0 + rng.choice(r1 - r0, size=min(per, r1 - r0), replace=False))
+    return np.unique(np.array(rows, dtype=np.int64))

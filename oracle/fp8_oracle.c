@@ -12,18 +12,20 @@
  * a 256-entry decode table (decode of each byte, computed once) and threads
  * over independent output elements.
  *
- * What the method computes (DeepSeek-V3 technical report, Section 3.3
- * "FP8 Training", as quoted on the source pages):
+ * What the method computes, as the source pages state it:
  *   - all GEMM inputs use E4M3 (4 exponent bits, 3 mantissa bits)
- *     (3.3.1 / 3.3.2, "E4M3 format on all tensors");
+ *     (jp-study.kr page, the passage adopting E4M3 on all tensors);
  *   - activations are grouped and scaled per 1x128 tile (one token, 128
- *     channels); weights per 128x128 block (Figure 7(a));
+ *     channels); weights per 128x128 block ("Should Fixing Deepseek Take 60
+ *     Steps?", Figure 7(a));
  *   - the scale maps each group's maximum absolute value, computed online,
- *     onto the largest finite E4M3 value (Section 3.3.2 "online
- *     quantization"; Section 3.3.1 on max-abs scaling);
+ *     onto the largest finite E4M3 value (why-be.why-be.co.kr page, online
+ *     max-abs passage; "Should Fixing Deepseek Take 60 Steps?", max-abs
+ *     scaling passage);
  *   - the GEMM consumes the FP8 operands, multiplies each partial result of
  *     a 128-wide K interval by the two block scales and accumulates in FP32
- *     ("promotion", Figure 7(b)); outputs are BF16 or FP32.
+ *     ("promotion", jp-study.kr page, Figure 7(b)); outputs are BF16 or FP32
+ *     ("Should Fixing Deepseek Take 60 Steps?", GEMM passage).
  *
  * Readings where the pages are silent (each is also listed in the design
  * notes of the repository):

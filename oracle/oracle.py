@@ -5,10 +5,12 @@ leg of the benchmark may import this module; the product package never does.
 
 This is a thin ctypes layer over ``liboracle.so`` (built from
 ``fp8_oracle.c`` by ``build_oracle()``); all arithmetic lives in the C file,
-whose header states the method and the readings it follows (DeepSeek-V3
-technical report, Section 3.3 "FP8 Training": E4M3 on all tensors, 1x128
-activation tiles and 128x128 weight blocks with online max-abs scales,
-Figure 7(a); per-128-K promotion into FP32, Figure 7(b)).
+whose header states the method and the readings it follows: E4M3 on all
+tensors (jp-study.kr page, E4M3-on-all-tensors passage); 1x128 activation
+tiles and 128x128 weight blocks ("Should Fixing Deepseek Take 60 Steps?",
+Figure 7(a)) with max-abs scales computed online (why-be.why-be.co.kr page,
+online max-abs passage); per-128-K promotion into FP32 (jp-study.kr page,
+Figure 7(b)).
 
 Arrays are numpy.  BF16 tensors are passed as their uint16 bit patterns.
 """
@@ -30,23 +32,34 @@ SCALE_BLOCK128, SCALE_ROW128 = 0, 1
 _lib = None
 
 
-def build_oracle() -> str:
-    """Compile fp8_oracle.c with gcc into liboracle.so (always rebuilds)."""
+def build_oracle(out: str | None = None, extra_flags=()) -> str:
+    """Compile fp8_oracle.c with gcc into liboracle.so, or into `out` with
+    extra compiler flags (the sanitizer build); always rebuilds."""
+    out = out or _LIB
     cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
-           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra",
-           _SRC, "-o", _LIB + ".tmp", "-lm"]
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra", *extra_flags,
+           _SRC, "-o", out + ".tmp", "-lm"]
     subprocess.check_call(cmd)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+# FP8Q_ORACLE_LIB names another build of fp8_oracle.c to load instead (the
+# sanitizer run of the oracle's own tests uses it).
+_ALT_LIB = os.environ.get("FP8Q_ORACLE_LIB")
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-        build_oracle()
-    lib = ctypes.CDLL(_LIB)
+    if _ALT_LIB:
+        path = _ALT_LIB
+    else:
+        path = _LIB
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build_oracle()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I = ctypes.c_int

@@ -2,9 +2,10 @@
 
 quant_small.txt: a 4x256 FP32 input (seeded, with a few large values and a
 zero group), its 1x128 codes and FP32 scale bit patterns; and a 256x128 input
-quantized as one 128x128 block pair.  Method: DeepSeek-V3 report, Section
-3.3.2, Figure 7(a) (1x128 activation tiles, 128x128 weight blocks, online
-max-abs scaling, E4M3 codes).
+quantized as one 128x128 block pair.  Method: 1x128 activation tiles and
+128x128 weight blocks ("Should Fixing Deepseek Take 60 Steps?", Figure 7(a)),
+max-abs scales computed online (why-be.why-be.co.kr page, online max-abs
+passage), E4M3 codes (jp-study.kr page, E4M3-on-all-tensors passage).
 
 Run:  python tests/golden/make_golden.py
 """

@@ -7,8 +7,8 @@ import pytest
 import torch
 
 from fp8_fine_grained_quant_amd import synth
-from helpers import (assert_same_bytes, check_gemm, codes, per_tile_elements, scale_bits, to_dev,
-                     union_elements)
+from helpers import (assert_same_bytes, check_gemm, codes, per_tile_elements, sample_elements,
+                     scale_bits, to_dev, union_elements)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,9 +67,11 @@ def test_grouped_moe_config(fq, oracle):
     """256 experts, 32768 tokens x top-8 (Zipf 1.1 popularity, 4 experts
     forced empty), X_g[262144,7168] * W_e[2048,7168]^T, BF16 out.  Checked:
     the 1x128 codes/scales of every grouped row (via the gather identity
-    quant(gather(X)) == gather(quant(X))), the 128x128 codes/scales of two
-    128-row blocks of every expert, and C on the first, last and two random
-    rows of every non-empty expert at 10 columns of those blocks."""
+    quant(gather(X)) == gather(quant(X))), the 128x128 codes and scales of
+    every expert weight in full, and C on 64 full rows, 64 full columns, 4096
+    random elements, the first and last output tiles, and -- for every
+    non-empty expert -- its first, last and 8 random rows in full (all 16
+    column blocks)."""
     rt = synth.moe_routing_default()
     E, N, K = synth.MOE_EXPERTS, 2048, 7168
     off = rt.offsets
@@ -94,39 +96,30 @@ def test_grouped_moe_config(fq, oracle):
     assert_same_bytes(codes(qa), qt_o[rt.token_of_row], "grouped activation codes")
     assert_same_bytes(scale_bits(sa), st_o[:, rt.token_of_row].view(np.uint32),
                       "grouped activation scales")
-    # weights: two 128-row blocks per expert
-    rng = np.random.default_rng(55)
-    blocks = [(e, 0) for e in range(E)] + [(e, int(rng.integers(1, N // 128))) for e in range(E)]
-    qw_h = codes(qw).reshape(E, N, K)
-    sw_h = scale_bits(sw).reshape(E, N // 128, K // 128)
-    qw_o = np.zeros((E, N, K), dtype=np.uint8)
-    sw_o = np.zeros((E, N // 128, K // 128), dtype=np.float32)
-    for e, b in blocks:
-        q, s, _ = oracle.quant_128x128(w[e, b * 128:(b + 1) * 128])
-        qw_o[e, b * 128:(b + 1) * 128] = q
-        sw_o[e, b] = s[0]
-        assert_same_bytes(qw_h[e, b * 128:(b + 1) * 128], q, f"expert {e} block {b} codes")
-        assert_same_bytes(sw_h[e, b], s[0].view(np.uint32), f"expert {e} block {b} scales")
-    # GEMM sample
-    ms, ns = [], []
+    del qa, sa
+    # weights: every expert in full, one expert at a time on the host
+    qw_o = np.empty((E, N, K), dtype=np.uint8)
+    sw_o = np.empty((E, N // 128, K // 128), dtype=np.float32)
+    qw3 = qw.view(E, N, K)
+    sw3 = sw.view(E, N // 128, K // 128)
     for e in range(E):
-        if rt.counts[e] == 0:
-            continue
-        rows = [off[e], off[e + 1] - 1] + list(rng.integers(off[e], off[e + 1], 2))
-        cols = [0, 127] + list(rng.integers(0, 128, 3))
-        bb = [b for ee, b in blocks if ee == e and b != 0][0]
-        cols += [bb * 128, bb * 128 + 127] + list(bb * 128 + rng.integers(0, 128, 3))
-        for r in rows:
-            for cc in cols:
-                ms.append(r)
-                ns.append(cc)
-    mi = np.array(ms, dtype=np.int64)
-    ni = np.array(ns, dtype=np.int64)
+        q, s, _ = oracle.quant_128x128(w[e])
+        qw_o[e], sw_o[e] = q, s
+        assert_same_bytes(codes(qw3[e]), q, f"expert {e} weight codes")
+        assert_same_bytes(scale_bits(sw3[e]), s.view(np.uint32), f"expert {e} weight scales")
+    print("moe: expert weight codes and scales bit-exact", flush=True)
+    del w
+    # GEMM sample: the dense sample, plus first, last and 8 random full rows
+    # of every non-empty expert
+    rows = synth.expert_rows(off, 55)
+    mi, ni = union_elements(N, sample_elements(Mt, N, 56),
+                            (np.repeat(rows, N), np.tile(np.arange(N), rows.size)))
     c_ref, s_ref = oracle.grouped_gemm_exact_elems(qt_o[rt.token_of_row], st_o[:, rt.token_of_row],
                                                    qw_o, sw_o, off, mi, ni)
     cg = c.float()[torch.from_numpy(mi).cuda(), torch.from_numpy(ni).cuda()].cpu().numpy()
     r = check_gemm(cg, c_ref, s_ref, True, "moe grouped")
-    print(f"moe: {mi.size} sampled elements, max |err| / tol = {r:.3g}")
+    print(f"moe: {mi.size} sampled elements ({rows.size} full expert rows), "
+          f"max |err| / tol = {r:.3g}")
 
 
 @pytest.mark.parametrize("K", [128, 384])

@@ -1,8 +1,8 @@
 """Pins for the oracle's E4M3 decode and encode.
 
 The pages fix the format only as "E4M3 (4-bit exponent and 3-bit mantissa)"
-used on all tensors (DeepSeek-V3 report, Section 3.3.2, mixed-precision
-framework; prior hybrid E4M3/E5M2 formats rejected).  The oracle reads it as
+used on all tensors (jp-study.kr page, the passage that sets aside the
+hybrid E4M3/E5M2 format of prior work for E4M3 everywhere).  The oracle reads it as
 OCP E4M3FN with round-to-nearest-even and saturation at 448; these tests pin
 that reading with closed forms, a brute-force nearest-value search written
 here, and PyTorch's own float8_e4m3fn cast.

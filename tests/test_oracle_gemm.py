@@ -1,9 +1,10 @@
 """Pins for the oracle's block-scaled GEMM.
 
-Method (DeepSeek-V3 report, Section 3.3.2, Figure 7(b)): the FP8 GEMM takes
-E4M3 operands; each 128-wide K interval's partial result is multiplied by the
-activation tile scale and the weight block scale and accumulated in FP32
-("promotion"); output BF16 or FP32.  The oracle computes the exact value of
+Method (jp-study.kr page, Figure 7(b); "Should Fixing Deepseek Take 60
+Steps?", GEMM passage): the FP8 GEMM takes E4M3 operands; each 128-wide K
+interval's partial result is multiplied by the activation tile scale and the
+weight block scale and accumulated in FP32 ("promotion"); output BF16 or
+FP32.  The oracle computes the exact value of
 that sum (fp64, each per-block partial exact); these tests check it against
 exact rational arithmetic, integer matmul and structural identities.
 """

@@ -1,9 +1,9 @@
 """Pins for the oracle's group quantizers.
 
-Method (DeepSeek-V3 report, Section 3.3.2, Figure 7(a)): activations are
-scaled per 1x128 tile (per token, per 128 channels), weights per 128x128
-block; each group's maximum absolute value is taken online and mapped onto the
-largest E4M3 value.  Readings: dequantization scale s = fl32(amax/448),
+Method ("Should Fixing Deepseek Take 60 Steps?", Figure 7(a)): activations
+are scaled per 1x128 tile (per token, per 128 channels), weights per 128x128
+block; each group's maximum absolute value is taken online (why-be.why-be.co.kr
+page, online max-abs passage) and mapped onto the largest E4M3 value.  Readings: dequantization scale s = fl32(amax/448),
 quantization multiplies by inv = min(fl32(448/amax), FLT_MAX).
 """
 import numpy as np
