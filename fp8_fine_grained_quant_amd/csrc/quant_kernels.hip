@@ -280,15 +280,18 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
             m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 16));
             m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 32));
         }
+        // column 8b+j of wave w at red[w*128 + 16j + b]: for each j the 16
+        // lanes (and, on the read side, the 16 column groups) touch 16
+        // consecutive words, free of bank conflicts
         if ((tid & 63) < 16) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) red[wave * 128 + 8 * b + j] = m[j];
+            for (int j = 0; j < 8; ++j) red[wave * 128 + 16 * j + b] = m[j];
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const int c = 8 * b + j;
-            uint32_t mm = max(max(red[c], red[128 + c]), max(red[256 + c], red[384 + c]));
+            const int e = 16 * j + b;   // column 8b+j
+            uint32_t mm = max(max(red[e], red[128 + e]), max(red[256 + e], red[384 + e]));
             float sc, iv;
             group_scale_rule<RULE>(__uint_as_float(mm), sc, iv);
             inv[j] = iv;
