@@ -51,6 +51,7 @@ namespace fp8q {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256;
 constexpr int BN = 256;
@@ -322,7 +323,11 @@ __device__ __forceinline__ Tile grouped_tile(const GemmParams& p, const int32_t*
 // instruction covers 4 whole 256-byte row segments.  The 16-byte chunks of a
 // buffer row are XOR-swizzled with the row (chunk ^ (row & 15)), which keeps
 // both the fragment-order writes and the row-order reads free of bank
-// conflicts.  Rows past m_end and columns past N are not written.
+// conflicts.  Rows past m_end and columns past N are not written.  Whole
+// 16-byte chunks go out as non-temporal stores: C is written once, and kept
+// out of the memory-side cache it leaves the A and B codes there for the
+// other tiles that re-read them (Fprop 858 -> 843 us, Dgrad 899 -> 891 us,
+// bitwise identical).
 template <int OUT, int NJ>
 __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)[4][NJ], uint8_t* buf,
                                            int64_t m_base, int64_t m_end, int64_t n_base, int lane) {
@@ -372,7 +377,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)
                 if (n >= N) continue;
                 float* cp = static_cast<float*>(p.c) + m * p.ldc + n;
                 if (n + 4 <= N) {
-                    *reinterpret_cast<uint4*>(cp) = v;
+                    __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(cp));
                 } else {
                     const float f[4] = {__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
                                         __uint_as_float(v.w)};
@@ -384,7 +389,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)
                 uint16_t* cp = static_cast<uint16_t*>(p.c) + m * p.ldc + n;
                 if (n + 8 <= N) {
                     if ((p.ldc & 7) == 0) {
-                        *reinterpret_cast<uint4*>(cp) = v;
+                        __builtin_nontemporal_store((u32x4){v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(cp));
                     } else {   // ldc % 8 == 4: rows alternate between 16- and 8-byte alignment
                         reinterpret_cast<uint2*>(cp)[0] = make_uint2(v.x, v.y);
                         reinterpret_cast<uint2*>(cp)[1] = make_uint2(v.z, v.w);
