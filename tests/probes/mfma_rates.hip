@@ -9,7 +9,10 @@
 //   16x16x128 : 32 v_mfma_scale_f32_16x16x128_f8f6f4 per step (unit E8M0
 //               scales), either accumulating in place or writing a fresh
 //               partial sum that an FP32 FMA promotes four instructions
-//               later (the FP32-scale GEMM's promotion);
+//               later (the FP32-scale GEMM's promotion), or -- "row x
+//               column", the weight-gradient GEMM's per-row scales on both
+//               operands -- with four products of a row scale and four
+//               column scales ahead of the four FMAs;
 //   32x32x64  : 16 v_mfma_scale_f32_32x32x64_f8f6f4, chained in pairs over
 //               one 128-wide K block, either in place or into a partial sum
 //               promoted with 16 FMAs two blocks later.
@@ -47,7 +50,7 @@ __device__ __forceinline__ v16f mf32(const v8i& a, const v8i& b, const v16f& c) 
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kOne, 0, kOne);
 }
 
-enum { k16InPlace, k16Promote, k32InPlace, k32Promote };
+enum { k16InPlace, k16Promote, k32InPlace, k32Promote, k16PromoteRow };
 
 template <int MODE, bool ONE_WAVE>
 __global__ __launch_bounds__(512, 1) void probe(const int* __restrict__ seed, float* __restrict__ out,
@@ -65,8 +68,12 @@ __global__ __launch_bounds__(512, 1) void probe(const int* __restrict__ seed, fl
     float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sc[i] = 1.0f + 0.001f * (float)(lane + i);
+    float4 cs[4];   // per-column scales of the four column blocks (row-scaled B)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        cs[j] = make_float4(1.f + 0.002f * lane, 1.f - 0.001f * j, 1.f + 0.003f * j, 0.5f + 0.001f * lane);
     float sum = 0.f;
-    if constexpr (MODE == k16InPlace || MODE == k16Promote) {
+    if constexpr (MODE == k16InPlace || MODE == k16Promote || MODE == k16PromoteRow) {
         v4f acc[4][8];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -88,14 +95,23 @@ __global__ __launch_bounds__(512, 1) void probe(const int* __restrict__ seed, fl
                         if (t >= D) {
                             const int u = t - D;
                             v4f& a = acc[u >> 2][4 * h + (u & 3)];
+                            if constexpr (MODE == k16PromoteRow) {
+                                // row scale times the lane's four column scales, then the FMAs
+                                const float4 c = cs[u & 3];
+                                a[0] = fmaf(part[u % R][0], sc[u >> 2] * c.x, a[0]);
+                                a[1] = fmaf(part[u % R][1], sc[u >> 2] * c.y, a[1]);
+                                a[2] = fmaf(part[u % R][2], sc[u >> 2] * c.z, a[2]);
+                                a[3] = fmaf(part[u % R][3], sc[u >> 2] * c.w, a[3]);
+                            } else {
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) a[r] = fmaf(part[u % R][r], sc[u >> 2], a[r]);
+                                for (int r = 0; r < 4; ++r) a[r] = fmaf(part[u % R][r], sc[u >> 2], a[r]);
+                            }
                         }
                     }
 #pragma unroll
                     for (int t = 0; t < 16 + D; ++t) {
                         if (t < 16) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                        if (t >= D) __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                        if (t >= D) __builtin_amdgcn_sched_group_barrier(0x002, MODE == k16PromoteRow ? 8 : 4, 0);
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
@@ -217,10 +233,12 @@ int main(int argc, char** argv) {
         run<k16Promote, false>("2 waves/SIMD 16x16x128 + FP32 promotion", dseed, dout, cus, iters);
         run<k32InPlace, false>("2 waves/SIMD 32x32x64 in place", dseed, dout, cus, iters);
         run<k32Promote, false>("2 waves/SIMD 32x32x64 + FP32 promotion", dseed, dout, cus, iters);
+        run<k16PromoteRow, false>("2 waves/SIMD 16x16x128 + row x column", dseed, dout, cus, iters);
         run<k16InPlace, true>("1 wave/SIMD 16x16x128 in place", dseed, dout, cus, iters);
         run<k16Promote, true>("1 wave/SIMD 16x16x128 + FP32 promotion", dseed, dout, cus, iters);
         run<k32InPlace, true>("1 wave/SIMD 32x32x64 in place", dseed, dout, cus, iters);
         run<k32Promote, true>("1 wave/SIMD 32x32x64 + FP32 promotion", dseed, dout, cus, iters);
+        run<k16PromoteRow, true>("1 wave/SIMD 16x16x128 + row x column", dseed, dout, cus, iters);
     }
     CHECK(hipFree(dseed));
     CHECK(hipFree(dout));

@@ -22,4 +22,4 @@ def test_mfma_rates_probe():
     print(res.stdout)
     assert res.returncode == 0, res.stdout + res.stderr
     rates = [float(m.group(1)) for m in re.finditer(r"(\d+\.\d+) of 5\.0 PFLOP/s", res.stdout)]
-    assert len(rates) == 16 and all(0.05 < r < 1.2 for r in rates), rates
+    assert len(rates) == 20 and all(0.05 < r < 1.2 for r in rates), rates
