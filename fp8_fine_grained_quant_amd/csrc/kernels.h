@@ -9,7 +9,7 @@
 namespace fp8q {
 
 enum { kF32 = 0, kBF16 = 1 };
-enum { kTileBlock = 0, kTileCols = 1 };
+enum { kTileBlock = 0, kTileCols = 1, kTileRows = 2 };
 enum { kScaleBlock128 = 0, kScaleRow128 = 1 };
 // Group scale rules: s = amax/448 (FP32), or the power of two 2^e with e the
 // smallest integer such that amax <= 448 * 2^e (an E8M0 exponent).
@@ -25,7 +25,8 @@ hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t col
 // 128x128 tiles of x[rows, cols] (row pitch ldx).  kTileBlock: one scale per
 // tile, s[ti*ceil(cols/128)+tj], codes to q (row-major) and/or qt
 // (transposed).  kTileCols: one scale per column per 128 rows,
-// s[ti*lds + col], codes to qt only.
+// s[ti*lds + col], codes to qt only.  kTileRows: one scale per row per 128
+// columns (1x128 groups), s[tj*lds + row], codes to q only.
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
                               float* s, int64_t lds, int rule, hipStream_t stream);

@@ -18,14 +18,17 @@
 //                        groups.
 //  quant_tile_kernel  -- 128x128 input tiles, thread (a, b) of 256 owning the
 //                        8x8 sub-tile rows 8a..8a+7, cols 8b..8b+7:
-//                        MODE_BLOCK: one scale per tile (weights), codes
+//                        kTileBlock: one scale per tile (weights), codes
 //                        stored row-major and/or transposed;
-//                        MODE_COLS: one scale per column over the tile's 128
+//                        kTileRows: one scale per row of the tile (1x128
+//                        groups, the 16 lanes of a DPP row), codes stored
+//                        row-major -- the 1x128 quantizer on matrices of
+//                        128 rows or more;
+//                        kTileCols: one scale per column over the tile's 128
 //                        rows (128x1 groups for the weight-gradient GEMM),
 //                        codes stored transposed.
-//                        The transposed store is an 8x8 byte transpose in
-//                        registers, so each thread writes 8-byte runs and
-//                        the 16 threads of a column run write 128 bytes.
+//                        A transposed store goes through LDS, so that every
+//                        wave writes whole 128-byte runs of output rows.
 #include <atomic>
 
 #include "device_common.h"
@@ -230,6 +233,26 @@ __device__ __forceinline__ uint32_t code_byte(uint32_t lo, uint32_t hi, int j) {
     return ((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4)))) & 0xFFu;
 }
 
+// Stores the 16 code bytes [c0, c0+16) of an output row (those below
+// `cols`); vec: 2 -- row start and pitch 16-byte aligned, 1 -- 8-byte, 0 --
+// neither.
+__device__ __forceinline__ void store16(uint8_t* row, int64_t c0, int64_t cols, uint4 v, int vec) {
+    if (vec == 2 && c0 + 16 <= cols) {
+        *reinterpret_cast<uint4*>(row + c0) = v;
+        return;
+    }
+    store8(row, c0, cols, v.x, v.y, vec == 1);
+    store8(row, c0 + 8, cols, v.z, v.w, vec == 1);
+}
+
+// The tile's transposed codes in LDS: output row c (input column c of the
+// tile) is 16 chunks of 8 bytes, chunk k holding input rows 8k..8k+7, stored
+// at position k ^ (c / 8 % 16).  The swizzle spreads the 16 lanes of a DPP
+// row, which write the same chunk of 16 different output rows, over all 32
+// banks; a chunk pair 2m, 2m+1 stays one aligned 16-byte word (swapped when
+// the swizzle is odd).
+constexpr int kTBufChunks = 128 * 16;
+
 template <int DT, int MODE, int RULE>
 __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ldx,
@@ -237,8 +260,9 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
                                                          uint8_t* __restrict__ qt, int64_t ldqt,
                                                          float* __restrict__ s, int64_t lds,
                                                          int64_t tiles_c, bool vin, bool vq,
-                                                         bool vqt) {
-    __shared__ uint32_t red[4 * 128];
+                                                         int vqt) {
+    __shared__ uint32_t red[MODE == kTileRows ? 1 : 4 * 128];
+    __shared__ __attribute__((aligned(16))) uint2 tbuf[MODE == kTileRows ? 1 : kTBufChunks];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int a = tid >> 4;   // sub-tile row group 0..15
@@ -251,6 +275,8 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
     float v[8][8];
     load_8x8<DT>(x, ldx, rows, cols, r0, c0, v, vin);
 
+    // inverse scales: inv[j] of column j (kTileBlock: all equal), or (kTileRows)
+    // inv[p] of row p
     float inv[8];
     if (MODE == kTileBlock) {
         uint32_t m = 0;
@@ -269,6 +295,24 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
         if (tid == 0) s[ti * tiles_c + tj] = sc;
 #pragma unroll
         for (int j = 0; j < 8; ++j) inv[j] = iv;
+    } else if (MODE == kTileRows) {
+        // row p of the sub-tile: its group is the row's 128 columns, held by
+        // the 16 lanes b = 0..15 of this DPP row
+        float sc[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            uint32_t m = 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) m = max(m, __float_as_uint(fabsf(v[p][j])));
+            m = row16_max_u32(m);
+            group_scale_rule<RULE>(__uint_as_float(m), sc[p], inv[p]);
+        }
+        // lane b < 8 stores the scale of row r0 + b: scale index [group][row]
+        float mine = sc[0];
+#pragma unroll
+        for (int p = 1; p < 8; ++p)
+            if (b == p) mine = sc[p];
+        if (b < 8 && r0 + b < rows) s[tj * lds + r0 + b] = mine;
     } else {
         // per-column max over the tile's 128 rows
         uint32_t m[8];
@@ -304,8 +348,13 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
-        lo[p] = enc4(v[p][0] * inv[0], v[p][1] * inv[1], v[p][2] * inv[2], v[p][3] * inv[3]);
-        hi[p] = enc4(v[p][4] * inv[4], v[p][5] * inv[5], v[p][6] * inv[6], v[p][7] * inv[7]);
+        if (MODE == kTileRows) {
+            lo[p] = enc4(v[p][0] * inv[p], v[p][1] * inv[p], v[p][2] * inv[p], v[p][3] * inv[p]);
+            hi[p] = enc4(v[p][4] * inv[p], v[p][5] * inv[p], v[p][6] * inv[p], v[p][7] * inv[p]);
+        } else {
+            lo[p] = enc4(v[p][0] * inv[0], v[p][1] * inv[1], v[p][2] * inv[2], v[p][3] * inv[3]);
+            hi[p] = enc4(v[p][4] * inv[4], v[p][5] * inv[5], v[p][6] * inv[6], v[p][7] * inv[7]);
+        }
     }
 
     if (q != nullptr) {
@@ -314,8 +363,9 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
             if (r0 + p < rows) store8(q + (r0 + p) * ldq, c0, cols, lo[p], hi[p], vq);
         }
     }
-    if (qt != nullptr) {
-        // transposed: output row c0+j holds bytes of input rows r0..r0+7
+    if (MODE != kTileRows && qt != nullptr) {
+        // transposed: output row c0+j holds bytes of input rows r0..r0+7,
+        // chunk a of LDS row 8b+j
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             uint32_t tlo = 0, thi = 0;
@@ -324,7 +374,21 @@ __global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict_
                 tlo |= code_byte(lo[p], hi[p], j) << (8 * p);
                 thi |= code_byte(lo[p + 4], hi[p + 4], j) << (8 * p);
             }
-            if (c0 + j < cols) store8(qt + (c0 + j) * ldqt, r0, rows, tlo, thi, vqt);
+            tbuf[(8 * b + j) * 16 + (a ^ b)] = make_uint2(tlo, thi);
+        }
+        __syncthreads();
+        // 128 output rows x 8 runs of 16 bytes: thread tid takes runs
+        // tid, tid + 256, ...; 8 consecutive lanes cover one output row
+        const int64_t oc0 = tj * 128, or0 = ti * 128;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            const int idx = it * 256 + tid;
+            const int c = idx >> 3;    // output row within the tile
+            const int k = idx & 7;     // 16-byte run: input rows 16k .. 16k+15
+            const int sw = (c >> 3) & 15;
+            const uint4 w = *reinterpret_cast<const uint4*>(&tbuf[c * 16 + ((2 * k) ^ (sw & ~1))]);
+            const uint4 run = (sw & 1) ? make_uint4(w.z, w.w, w.x, w.y) : w;
+            if (oc0 + c < cols) store16(qt + (oc0 + c) * ldqt, or0 + 16 * k, rows, run, vqt);
         }
     }
 }
@@ -397,6 +461,11 @@ static hipError_t launch_rows_t(const void* x, int64_t rows, int64_t cols, int64
 hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, int rule,
                              hipStream_t stream) {
+    // 128 rows or more: 128x128 tiles (kTileRows), whose loads and stores
+    // are those of the weight quantizer; fewer rows: the row-striding kernel
+    if (rows >= 128 && (rows + 127) / 128 * ((cols + 127) / 128) <= 0x7FFFFFFF)
+        return launch_quant_tiles(x, dtype, kTileRows, rows, cols, ldx, q, ldq, nullptr, 0, s, lds,
+                                  rule, stream);
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vout = is_aligned(q, 8) && ldq % 8 == 0;
@@ -418,7 +487,10 @@ hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, 
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vq = q != nullptr && is_aligned(q, 8) && ldq % 8 == 0;
-    const bool vqt = qt != nullptr && is_aligned(qt, 8) && ldqt % 8 == 0;
+    const int vqt = qt == nullptr ? 0
+                    : (is_aligned(qt, 16) && ldqt % 16 == 0) ? 2
+                    : (is_aligned(qt, 8) && ldqt % 8 == 0) ? 1
+                                                           : 0;
 #define FP8Q_LAUNCH_TILE(DT, MD, RL)                                                     \
     hipLaunchKernelGGL((quant_tile_kernel<DT, MD, RL>), grid, block, 0, stream, x, rows, cols, \
                        ldx, q, ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
@@ -427,13 +499,15 @@ hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, 
         if (rule == kRulePow2) FP8Q_LAUNCH_TILE(DT, MD, kRulePow2); \
         else FP8Q_LAUNCH_TILE(DT, MD, kRuleFP32);              \
     } while (0)
-    if (dtype == kBF16) {
-        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(kBF16, kTileBlock);
-        else FP8Q_LAUNCH_TILE_RULE(kBF16, kTileCols);
-    } else {
-        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(kF32, kTileBlock);
-        else FP8Q_LAUNCH_TILE_RULE(kF32, kTileCols);
-    }
+#define FP8Q_LAUNCH_TILE_MODE(DT)                                         \
+    do {                                                                  \
+        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(DT, kTileBlock);    \
+        else if (mode == kTileRows) FP8Q_LAUNCH_TILE_RULE(DT, kTileRows); \
+        else FP8Q_LAUNCH_TILE_RULE(DT, kTileCols);                        \
+    } while (0)
+    if (dtype == kBF16) FP8Q_LAUNCH_TILE_MODE(kBF16);
+    else FP8Q_LAUNCH_TILE_MODE(kF32);
+#undef FP8Q_LAUNCH_TILE_MODE
 #undef FP8Q_LAUNCH_TILE_RULE
 #undef FP8Q_LAUNCH_TILE
     return hipGetLastError();
