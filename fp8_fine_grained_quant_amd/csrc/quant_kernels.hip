@@ -20,7 +20,7 @@
 //                        8x8 sub-tile rows 8a..8a+7, cols 8b..8b+7:
 //                        kTileBlock: one scale per tile (weights), codes
 //                        stored row-major and/or transposed;
-//                        kTileRows: one scale per row of the tile (1x128
+//                        kTileRows: 32x128 tiles, one scale per row (1x128
 //                        groups, the 16 lanes of a DPP row), codes stored
 //                        row-major -- the 1x128 quantizer on matrices of
 //                        128 rows or more;
@@ -253,23 +253,32 @@ __device__ __forceinline__ void store16(uint8_t* row, int64_t c0, int64_t cols, 
 // the swizzle is odd).
 constexpr int kTBufChunks = 128 * 16;
 
-template <int DT, int MODE, int RULE>
-__global__ __launch_bounds__(256) void quant_tile_kernel(const void* __restrict__ x, int64_t rows,
+// Tile height of the 1x128 mode: a group needs a tile's full 128 columns but
+// not its 128 rows, and shorter tiles leave a smaller last round of
+// workgroups (one-wave workgroups: A [8192,7168] 34.2 -> 33.5 us, tokens
+// [32768,7168] 112.1 -> 110.6 us against 128-row tiles; 64 rows in between).
+constexpr int kRowTileH = 32;
+
+// TH: tile height (rows), 128 except in kTileRows mode; the workgroup has
+// 2*TH threads.
+template <int DT, int MODE, int RULE, int TH = 128>
+__global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restrict__ x, int64_t rows,
                                                          int64_t cols, int64_t ldx,
                                                          uint8_t* __restrict__ q, int64_t ldq,
                                                          uint8_t* __restrict__ qt, int64_t ldqt,
                                                          float* __restrict__ s, int64_t lds,
                                                          int64_t tiles_c, bool vin, bool vq,
                                                          int vqt) {
+    static_assert(TH == 128 || MODE == kTileRows, "only 1x128 groups allow short tiles");
     __shared__ uint32_t red[MODE == kTileRows ? 1 : 4 * 128];
     __shared__ __attribute__((aligned(16))) uint2 tbuf[MODE == kTileRows ? 1 : kTBufChunks];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
-    const int a = tid >> 4;   // sub-tile row group 0..15
+    const int a = tid >> 4;   // sub-tile row group 0..TH/8-1
     const int b = tid & 15;   // sub-tile col group 0..15
     const int64_t ti = blockIdx.x / tiles_c;
     const int64_t tj = blockIdx.x - ti * tiles_c;
-    const int64_t r0 = ti * 128 + 8 * a;
+    const int64_t r0 = ti * TH + 8 * a;
     const int64_t c0 = tj * 128 + 8 * b;
 
     float v[8][8];
@@ -461,9 +470,10 @@ static hipError_t launch_rows_t(const void* x, int64_t rows, int64_t cols, int64
 hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
                              uint8_t* q, int64_t ldq, float* s, int64_t lds, int rule,
                              hipStream_t stream) {
-    // 128 rows or more: 128x128 tiles (kTileRows), whose loads and stores
-    // are those of the weight quantizer; fewer rows: the row-striding kernel
-    if (rows >= 128 && (rows + 127) / 128 * ((cols + 127) / 128) <= 0x7FFFFFFF)
+    // 128 rows or more: kRowTileH x 128 tiles (kTileRows), whose loads and
+    // stores are those of the weight quantizer; fewer rows: the row-striding
+    // kernel
+    if (rows >= 128 && (rows + kRowTileH - 1) / kRowTileH * ((cols + 127) / 128) <= 0x7FFFFFFF)
         return launch_quant_tiles(x, dtype, kTileRows, rows, cols, ldx, q, ldq, nullptr, 0, s, lds,
                                   rule, stream);
     const int64_t esz = dtype == kBF16 ? 2 : 4;
@@ -482,8 +492,9 @@ hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t col
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
                               float* s, int64_t lds, int rule, hipStream_t stream) {
-    const int64_t tr = (rows + 127) / 128, tc = (cols + 127) / 128;
-    dim3 grid((unsigned)(tr * tc)), block(256);
+    const int64_t th = mode == kTileRows ? kRowTileH : 128;
+    const int64_t tr = (rows + th - 1) / th, tc = (cols + 127) / 128;
+    dim3 grid((unsigned)(tr * tc)), block((unsigned)(2 * th));
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vq = q != nullptr && is_aligned(q, 8) && ldq % 8 == 0;
@@ -491,9 +502,9 @@ hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, 
                     : (is_aligned(qt, 16) && ldqt % 16 == 0) ? 2
                     : (is_aligned(qt, 8) && ldqt % 8 == 0) ? 1
                                                            : 0;
-#define FP8Q_LAUNCH_TILE(DT, MD, RL)                                                     \
-    hipLaunchKernelGGL((quant_tile_kernel<DT, MD, RL>), grid, block, 0, stream, x, rows, cols, \
-                       ldx, q, ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
+#define FP8Q_LAUNCH_TILE(DT, MD, RL)                                                          \
+    hipLaunchKernelGGL((quant_tile_kernel<DT, MD, RL, MD == kTileRows ? kRowTileH : 128>), grid, \
+                       block, 0, stream, x, rows, cols, ldx, q, ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
 #define FP8Q_LAUNCH_TILE_RULE(DT, MD)                          \
     do {                                                       \
         if (rule == kRulePow2) FP8Q_LAUNCH_TILE(DT, MD, kRulePow2); \
