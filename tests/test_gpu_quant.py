@@ -77,6 +77,38 @@ def test_quant_1x128_padded_leading_dims_untouched(fq, oracle):
     assert torch.isnan(s[:, 40:]).all(), "padding of s was written"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_1x128_tile_path_edges(fq, oracle, dtype):
+    """Row counts around the switch from the row-striding kernel (fewer than
+    128 rows) to 32x128 tiles, ragged last tiles in both directions, and
+    inputs and outputs that only allow element accesses: an input view one
+    element off its 16-byte alignment, a row pitch that is not a multiple of
+    16 bytes, and code rows whose pitch is not a multiple of 8."""
+    rng = np.random.default_rng(77 if dtype == "f32" else 78)
+    for R, C in [(127, 128), (128, 128), (129, 129), (159, 1000), (160, 256), (161, 385)]:
+        x = (rng.standard_normal((R, C)) * np.exp(rng.uniform(-6, 6, (R, 1)))).astype(np.float32)
+        if dtype == "bf16":
+            x = synth.f32_to_bf16_bits(x)
+        _check_1x128(fq, oracle, x, what=f"{R}x{C} {dtype}")
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    R, C = 200, 300
+    x = (rng.standard_normal((R, C)) * np.exp(rng.uniform(-6, 6, (R, 1)))).astype(np.float32)
+    xo = to_dev(x).to(tdt)
+    xv = xo.float().cpu().numpy()
+    qo, so = oracle.quant_1x128(xv)
+    # input one element past a 16-byte boundary, row pitch C+3 elements
+    buf = torch.zeros((R, C + 3), dtype=tdt, device="cuda")
+    buf[:, 1:C + 1] = xo
+    q = torch.full((R, C + 5), 0x5A, dtype=torch.uint8, device="cuda")   # code pitch not a multiple of 8
+    s = torch.full(((C + 127) // 128, R + 3), float("nan"), dtype=torch.float32, device="cuda")
+    fq.fp8_quant_1x128(buf[:, 1:C + 1], q=q[:, :C], s=s[:, :R])
+    torch.cuda.synchronize()
+    assert_same_bytes(codes(q)[:, :C], qo, f"unaligned {dtype} codes")
+    assert np.all(codes(q)[:, C:] == 0x5A), "row padding of q was written"
+    assert_same_bytes(scale_bits(s)[:, :R], so.view(np.uint32), f"unaligned {dtype} scales")
+    assert torch.isnan(s[:, R:]).all(), "padding of s was written"
+
+
 def test_quant_1x128_special_groups(fq, oracle):
     x = np.zeros((8, 512), dtype=np.float32)
     x[1, :128] = -0.0                                  # all negative zero
