@@ -50,9 +50,9 @@ int quant_1x128_impl(const void* x, int x_dtype, int64_t rows, int64_t cols, int
     }
     if (xs_r == 1 && (xs_c >= rows || cols == 1)) {
         // Stored transposed: physical tensor [cols, rows] with row pitch xs_c;
-        // 128x1 groups along its rows, codes written transposed.  One
-        // workgroup per 128x128 tile.
-        if ((rows + 127) / 128 * ((cols + 127) / 128) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
+        // 128x1 groups along its rows, codes written transposed, in 128x256
+        // tiles (fewer than 2^31 of them).
+        if ((cols + 127) / 128 * ((rows + 255) / 256) > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;
         const int64_t ldx = cols == 1 ? rows : xs_c;
         return launch_status(fp8q::launch_quant_tiles(x, x_dtype, fp8q::kTileCols, cols, rows,
                                                       ldx, nullptr, 0, q, ldq, s, lds, rule,

@@ -25,7 +25,7 @@ hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t col
 // 128x128 tiles of x[rows, cols] (row pitch ldx).  kTileBlock: one scale per
 // tile, s[ti*ceil(cols/128)+tj], codes to q (row-major) and/or qt
 // (transposed).  kTileCols: one scale per column per 128 rows,
-// s[ti*lds + col], codes to qt only.  kTileRows: one scale per row per 128
+// s[ti*lds + col], codes to qt only (128x256 tiles).  kTileRows: one scale per row per 128
 // columns (1x128 groups), s[tj*lds + row], codes to q only.
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,

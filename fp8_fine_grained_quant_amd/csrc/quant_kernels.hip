@@ -23,12 +23,16 @@
 //                        kTileRows: 32x128 tiles, one scale per row (1x128
 //                        groups, the 16 lanes of a DPP row), codes stored
 //                        row-major -- the 1x128 quantizer on matrices of
-//                        128 rows or more;
-//                        kTileCols: one scale per column over the tile's 128
-//                        rows (128x1 groups for the weight-gradient GEMM),
-//                        codes stored transposed.
-//                        A transposed store goes through LDS, so that every
-//                        wave writes whole 128-byte runs of output rows.
+//                        128 rows or more.
+//                        The transposed copy of kTileBlock goes through LDS,
+//                        so that every wave writes whole 128-byte runs of
+//                        output rows.
+//  quant_cols_kernel  -- 128x1 groups (one scale per column over 128 rows,
+//                        for the weight-gradient GEMM), codes stored
+//                        transposed: 128x256 tiles, one 128x64 strip per
+//                        wave, a column's 128 rows in one wave, and each
+//                        lane's 16 codes of a column one 16-byte run of its
+//                        output row.
 #include <atomic>
 
 #include "device_common.h"
@@ -200,24 +204,24 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 // 128x128 tiles: block scales (weights) or column scales (128x1 groups)
 // ---------------------------------------------------------------------------
 
-// Reads the 8x8 sub-tile rows r0..r0+7, cols c0..c0+7 of a row-major matrix;
-// elements outside [rows, cols] read as 0.  An interior sub-tile of an
-// aligned matrix issues its eight row loads before unpacking any.
-template <int DT>
-__device__ __forceinline__ void load_8x8(const void* x, int64_t ldx, int64_t rows, int64_t cols,
-                                         int64_t r0, int64_t c0, float v[8][8], bool vin) {
+// Reads the NRx8 sub-tile rows r0..r0+NR-1, cols c0..c0+7 of a row-major
+// matrix; elements outside [rows, cols] read as 0.  An interior sub-tile of
+// an aligned matrix issues all of its row loads before unpacking any.
+template <int DT, int NR>
+__device__ __forceinline__ void load_rows8(const void* x, int64_t ldx, int64_t rows, int64_t cols,
+                                           int64_t r0, int64_t c0, float v[NR][8], bool vin) {
     const size_t esz = DT == kBF16 ? 2 : 4;
-    if (vin && r0 + 8 <= rows && c0 + 8 <= cols) {
-        Run8 raw[8];
+    if (vin && r0 + NR <= rows && c0 + 8 <= cols) {
+        Run8 raw[NR];
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
+        for (int p = 0; p < NR; ++p)
             issue8<DT>(static_cast<const char*>(x) + (size_t)(r0 + p) * (size_t)ldx * esz, c0, raw[p]);
 #pragma unroll
-        for (int p = 0; p < 8; ++p) unpack8<DT>(raw[p], v[p]);
+        for (int p = 0; p < NR; ++p) unpack8<DT>(raw[p], v[p]);
         return;
     }
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < NR; ++p) {
         if (r0 + p < rows) {
             load8_elems<DT>(static_cast<const char*>(x) + (size_t)(r0 + p) * (size_t)ldx * esz, c0,
                             cols, v[p]);
@@ -269,8 +273,9 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
                                                          float* __restrict__ s, int64_t lds,
                                                          int64_t tiles_c, bool vin, bool vq,
                                                          int vqt) {
+    static_assert(MODE == kTileBlock || MODE == kTileRows, "128x1 groups: quant_cols_kernel");
     static_assert(TH == 128 || MODE == kTileRows, "only 1x128 groups allow short tiles");
-    __shared__ uint32_t red[MODE == kTileRows ? 1 : 4 * 128];
+    __shared__ uint32_t red[MODE == kTileRows ? 1 : 4];
     __shared__ __attribute__((aligned(16))) uint2 tbuf[MODE == kTileRows ? 1 : kTBufChunks];
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -282,12 +287,12 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
     const int64_t c0 = tj * 128 + 8 * b;
 
     float v[8][8];
-    load_8x8<DT>(x, ldx, rows, cols, r0, c0, v, vin);
+    load_rows8<DT, 8>(x, ldx, rows, cols, r0, c0, v, vin);
 
-    // inverse scales: inv[j] of column j (kTileBlock: all equal), or (kTileRows)
+    // inverse scales: kTileBlock -- inv[j] of column j, all equal; kTileRows --
     // inv[p] of row p
     float inv[8];
-    if (MODE == kTileBlock) {
+    if constexpr (MODE == kTileBlock) {
         uint32_t m = 0;
 #pragma unroll
         for (int p = 0; p < 8; ++p)
@@ -304,7 +309,7 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
         if (tid == 0) s[ti * tiles_c + tj] = sc;
 #pragma unroll
         for (int j = 0; j < 8; ++j) inv[j] = iv;
-    } else if (MODE == kTileRows) {
+    } else {
         // row p of the sub-tile: its group is the row's 128 columns, held by
         // the 16 lanes b = 0..15 of this DPP row
         float sc[8];
@@ -322,35 +327,6 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
         for (int p = 1; p < 8; ++p)
             if (b == p) mine = sc[p];
         if (b < 8 && r0 + b < rows) s[tj * lds + r0 + b] = mine;
-    } else {
-        // per-column max over the tile's 128 rows
-        uint32_t m[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            m[j] = 0;
-#pragma unroll
-            for (int p = 0; p < 8; ++p) m[j] = max(m[j], __float_as_uint(fabsf(v[p][j])));
-            m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 16));
-            m[j] = max(m[j], (uint32_t)__shfl_xor((int)m[j], 32));
-        }
-        // column 8b+j of wave w at red[w*128 + 16j + b]: for each j the 16
-        // lanes (and, on the read side, the 16 column groups) touch 16
-        // consecutive words, free of bank conflicts
-        if ((tid & 63) < 16) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) red[wave * 128 + 16 * j + b] = m[j];
-        }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int e = 16 * j + b;   // column 8b+j
-            uint32_t mm = max(max(red[e], red[128 + e]), max(red[256 + e], red[384 + e]));
-            float sc, iv;
-            group_scale_rule<RULE>(__uint_as_float(mm), sc, iv);
-            inv[j] = iv;
-            // logical output row = input column; scale index [tile row][column]
-            if (a == 0 && c0 + j < cols) s[ti * lds + c0 + j] = sc;
-        }
     }
 
     // codes: row p of the sub-tile as two dwords
@@ -372,7 +348,7 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
             if (r0 + p < rows) store8(q + (r0 + p) * ldq, c0, cols, lo[p], hi[p], vq);
         }
     }
-    if (MODE != kTileRows && qt != nullptr) {
+    if (MODE == kTileBlock && qt != nullptr) {
         // transposed: output row c0+j holds bytes of input rows r0..r0+7,
         // chunk a of LDS row 8b+j
 #pragma unroll
@@ -399,6 +375,77 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
             const uint4 run = (sw & 1) ? make_uint4(w.z, w.w, w.x, w.y) : w;
             if (oc0 + c < cols) store16(qt + (oc0 + c) * ldqt, or0 + 16 * k, rows, run, vqt);
         }
+    }
+}
+
+// 128x1 groups (one scale per column over 128 rows: the weight-gradient
+// operands), codes stored transposed.  A workgroup takes a 128-row x
+// 256-column tile, each of its four waves a 128 x 64 strip; lane (a, b) =
+// (lane / 8, lane % 8) of a wave owns rows 16a..16a+15 and columns
+// 8b..8b+7 of the strip.  So:
+//  - a wave's load instruction reads 8 rows, each a whole 128-byte segment
+//    (BF16), and the four waves read the rows' adjacent segments together;
+//  - a column's 128 rows lie in one wave, and its max takes three lane
+//    exchanges over the 8 row groups (no LDS, no barrier);
+//  - the 16 codes a lane holds of one column are 16 consecutive bytes of
+//    that column's output row: one 16-byte store, and the 8 lanes of a
+//    column group write one whole 128-byte output segment.
+// A/B against 128x128 tiles with an LDS exchange, bitwise identical: X^T
+// [7168 x 8192 tokens] 37.8 -> 34.3 us, dY^T [2048 x 8192] 13.6 -> 11.7 us;
+// one-wave workgroups (128 x 64 tiles) lose on X^T (40.6 us), and eight-wave
+// ones too (40.8 us).  Three waves per SIMD (168 VGPRs) against two: X^T 35.8
+// -> 34.3 us; four spill.
+constexpr int kColStripW = 64;
+constexpr int kColWaves = 4;
+
+template <int DT, int RULE>
+__global__ __launch_bounds__(64 * kColWaves, 3) void quant_cols_kernel(
+        const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* __restrict__ qt,
+        int64_t ldqt, float* __restrict__ s, int64_t lds, int64_t tiles_c, bool vin, int vqt, bool vs) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int a = lane >> 3;   // row group 0..7
+    const int b = lane & 7;    // column group 0..7
+    const int64_t ti = blockIdx.x / tiles_c;
+    const int64_t tj = blockIdx.x - ti * tiles_c;
+    const int64_t r0 = ti * 128 + 16 * a;
+    const int64_t c0 = (tj * kColWaves + wave) * kColStripW + 8 * b;
+
+    float v[16][8];
+    load_rows8<DT, 16>(x, ldx, rows, cols, r0, c0, v, vin);
+
+    float sc[8], inv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int p = 0; p < 16; ++p) m = max(m, __float_as_uint(fabsf(v[p][j])));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 8));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+        m = max(m, (uint32_t)__shfl_xor((int)m, 32));
+        group_scale_rule<RULE>(__uint_as_float(m), sc[j], inv[j]);
+    }
+    // logical output row = input column; scale index [tile row][column]
+    if (a == 0) {
+        float* sp = s + ti * lds + c0;
+        if (vs && c0 + 8 <= cols) {
+            reinterpret_cast<float4*>(sp)[0] = make_float4(sc[0], sc[1], sc[2], sc[3]);
+            reinterpret_cast<float4*>(sp)[1] = make_float4(sc[4], sc[5], sc[6], sc[7]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (c0 + j < cols) sp[j] = sc[j];
+        }
+    }
+    // output row c0+j, bytes r0..r0+15: the column's codes in row order
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        uint32_t w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            w[q] = enc4(v[4 * q][j] * inv[j], v[4 * q + 1][j] * inv[j], v[4 * q + 2][j] * inv[j],
+                        v[4 * q + 3][j] * inv[j]);
+        if (c0 + j < cols) store16(qt + (c0 + j) * ldqt, r0, rows, make_uint4(w[0], w[1], w[2], w[3]), vqt);
     }
 }
 
@@ -492,9 +539,6 @@ hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t col
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
                               float* s, int64_t lds, int rule, hipStream_t stream) {
-    const int64_t th = mode == kTileRows ? kRowTileH : 128;
-    const int64_t tr = (rows + th - 1) / th, tc = (cols + 127) / 128;
-    dim3 grid((unsigned)(tr * tc)), block((unsigned)(2 * th));
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
     const bool vq = q != nullptr && is_aligned(q, 8) && ldq % 8 == 0;
@@ -502,6 +546,27 @@ hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, 
                     : (is_aligned(qt, 16) && ldqt % 16 == 0) ? 2
                     : (is_aligned(qt, 8) && ldqt % 8 == 0) ? 1
                                                            : 0;
+    if (mode == kTileCols) {
+        const int64_t tw = kColStripW * kColWaves;
+        const int64_t tc = (cols + tw - 1) / tw;
+        const dim3 grid((unsigned)((rows + 127) / 128 * tc)), block(64 * kColWaves);
+        const bool vs = is_aligned(s, 16) && lds % 4 == 0;
+#define FP8Q_LAUNCH_COLS(DT, RL)                                                                   \
+    hipLaunchKernelGGL((quant_cols_kernel<DT, RL>), grid, block, 0, stream, x, rows, cols, ldx, qt, \
+                       ldqt, s, lds, tc, vin, vqt, vs)
+        if (dtype == kBF16) {
+            if (rule == kRulePow2) FP8Q_LAUNCH_COLS(kBF16, kRulePow2);
+            else FP8Q_LAUNCH_COLS(kBF16, kRuleFP32);
+        } else {
+            if (rule == kRulePow2) FP8Q_LAUNCH_COLS(kF32, kRulePow2);
+            else FP8Q_LAUNCH_COLS(kF32, kRuleFP32);
+        }
+#undef FP8Q_LAUNCH_COLS
+        return hipGetLastError();
+    }
+    const int64_t th = mode == kTileRows ? kRowTileH : 128;
+    const int64_t tr = (rows + th - 1) / th, tc = (cols + 127) / 128;
+    dim3 grid((unsigned)(tr * tc)), block((unsigned)(2 * th));
 #define FP8Q_LAUNCH_TILE(DT, MD, RL)                                                          \
     hipLaunchKernelGGL((quant_tile_kernel<DT, MD, RL, MD == kTileRows ? kRowTileH : 128>), grid, \
                        block, 0, stream, x, rows, cols, ldx, q, ldq, qt, ldqt, s, lds, tc, vin, vq, vqt)
@@ -510,11 +575,10 @@ hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, 
         if (rule == kRulePow2) FP8Q_LAUNCH_TILE(DT, MD, kRulePow2); \
         else FP8Q_LAUNCH_TILE(DT, MD, kRuleFP32);              \
     } while (0)
-#define FP8Q_LAUNCH_TILE_MODE(DT)                                         \
-    do {                                                                  \
-        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(DT, kTileBlock);    \
-        else if (mode == kTileRows) FP8Q_LAUNCH_TILE_RULE(DT, kTileRows); \
-        else FP8Q_LAUNCH_TILE_RULE(DT, kTileCols);                        \
+#define FP8Q_LAUNCH_TILE_MODE(DT)                                      \
+    do {                                                               \
+        if (mode == kTileBlock) FP8Q_LAUNCH_TILE_RULE(DT, kTileBlock); \
+        else FP8Q_LAUNCH_TILE_RULE(DT, kTileRows);                     \
     } while (0)
     if (dtype == kBF16) FP8Q_LAUNCH_TILE_MODE(kBF16);
     else FP8Q_LAUNCH_TILE_MODE(kF32);
