@@ -232,6 +232,18 @@ __device__ __forceinline__ void load_rows8(const void* x, int64_t ldx, int64_t r
     }
 }
 
+// Tile of workgroup b in a one-tile-per-workgroup grid of n: workgroups are
+// dealt to the 8 XCDs round-robin (b % 8), so XCD x takes the contiguous
+// tiles [start(x), start(x) + count(x)) instead of every eighth one, and
+// tiles that are neighbours in a row run on one XCD at about the same time.
+// A bijection on [0, n): XCD x has count(x) = n/8 + (x < n%8) workgroups.
+// (128x128 blocks of W_e [524288,7168]: 2110 -> 1946 us; tokens [32768,7168]
+// 110.8 -> 107.6 us; the 128x1 kernel is 2 % faster without it.)
+__device__ __forceinline__ uint32_t xcd_tile(uint32_t b, uint32_t n) {
+    const uint32_t x = b & 7, i = b >> 3, q = n >> 3, r = n & 7;
+    return x * q + min(x, r) + i;
+}
+
 // Byte j of the 8-byte row code (lo: bytes 0..3, hi: bytes 4..7).
 __device__ __forceinline__ uint32_t code_byte(uint32_t lo, uint32_t hi, int j) {
     return ((j < 4 ? lo >> (8 * j) : hi >> (8 * (j - 4)))) & 0xFFu;
@@ -281,8 +293,9 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
     const int wave = tid >> 6;
     const int a = tid >> 4;   // sub-tile row group 0..TH/8-1
     const int b = tid & 15;   // sub-tile col group 0..15
-    const int64_t ti = blockIdx.x / tiles_c;
-    const int64_t tj = blockIdx.x - ti * tiles_c;
+    const uint32_t tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t ti = tile / tiles_c;
+    const int64_t tj = tile - ti * tiles_c;
     const int64_t r0 = ti * TH + 8 * a;
     const int64_t c0 = tj * 128 + 8 * b;
 
