@@ -109,6 +109,33 @@ def test_quant_1x128_tile_path_edges(fq, oracle, dtype):
     assert torch.isnan(s[:, R:]).all(), "padding of s was written"
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_128x1_edges(fq, oracle, dtype):
+    """128x1 groups (the transposed view) on ragged 128-row groups and
+    ragged 256-column tiles, with an input view one element off its 16-byte
+    alignment and padded pitches for the input, the transposed codes (not a
+    multiple of 8) and the scales (not a multiple of 4): element accesses
+    throughout, and the padding left untouched."""
+    rng = np.random.default_rng(91 if dtype == "f32" else 92)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for T, C in [(300, 300), (128, 257), (129, 64)]:
+        x = (rng.standard_normal((T, C)) * np.exp(rng.uniform(-6, 6, (1, C)))).astype(np.float32)
+        xo = to_dev(x).to(tdt)
+        qo, so = oracle.quant_1x128(xo.float().cpu().numpy(), transposed=True)
+        buf = torch.zeros((T, C + 3), dtype=tdt, device="cuda")
+        buf[:, 1:C + 1] = xo
+        g = (T + 127) // 128
+        q = torch.full((C, T + 5), 0x5A, dtype=torch.uint8, device="cuda")
+        sc = torch.full((g, C + 3), float("nan"), dtype=torch.float32, device="cuda")
+        fq.fp8_quant_1x128(buf[:, 1:C + 1], transposed=True, q=q[:, :T], s=sc[:, :C])
+        torch.cuda.synchronize()
+        what = f"128x1 {T}x{C} {dtype}"
+        assert_same_bytes(codes(q)[:, :T], qo, what + " codes")
+        assert np.all(codes(q)[:, T:] == 0x5A), what + ": row padding of q was written"
+        assert_same_bytes(scale_bits(sc)[:, :C], so.view(np.uint32), what + " scales")
+        assert torch.isnan(sc[:, C:]).all(), what + ": padding of s was written"
+
+
 def test_quant_1x128_special_groups(fq, oracle):
     x = np.zeros((8, 512), dtype=np.float32)
     x[1, :128] = -0.0                                  # all negative zero
