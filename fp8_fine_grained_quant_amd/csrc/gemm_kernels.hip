@@ -20,9 +20,10 @@
 // Design (256x256 output tiles; a persistent workgroup of 8 waves, 2 per
 // SIMD, on each compute unit loops over its tiles):
 //  * K step 128 = exactly one scale block, so each K step is one
-//    v_mfma_scale_f32_16x16x128_f8f6f4 per 16x16 output block (scale
-//    operands set to 1.0; the FP32 block scales are applied by the
-//    promotion FMA).
+//    16x16x128 FP8 matrix instruction per 16x16 output block: the plain
+//    v_mfma_f32_16x16x128_f8f6f4 with FP32 block scales, which the
+//    promotion FMA applies, or v_mfma_scale_f32_16x16x128_f8f6f4 carrying
+//    power-of-two scales.
 //  * A and B K-slabs (256x128 bytes each) go HBM -> LDS with
 //    global_load_lds_dwordx4 (no VGPR staging), double buffered: the next
 //    slab streams in while the current one is multiplied.  Rows are 128
@@ -61,7 +62,6 @@ constexpr int kWaveM = 64;
 constexpr int kSlabBytes = BM * BK;          // one operand, one stage
 constexpr int kStageBytes = 2 * kSlabBytes;  // A + B
 constexpr int kGroupM = 8;                   // tile rows per swizzle group
-constexpr unsigned kOneE8M0 = 127;           // MFMA block scale 2^0
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -121,9 +121,15 @@ __device__ __forceinline__ v8i frag32(const uint8_t* __restrict__ slab, int bloc
                  (int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
 }
 
+// The partial sum of one 128-wide K block, unscaled.  Zero scale operands
+// make the compiler emit the plain v_mfma_f32_16x16x128_f8f6f4, which has
+// no scale operands; a probe found it bitwise equal to the scaled form with
+// unit (E8M0 127) scales on 262,144 random outputs, and it issues faster
+// (Fprop 781.6 -> 774.8 us, Dgrad 821.6 -> 813.7 us, Wgrad 118.8 -> 115.1
+// us, bitwise identical).
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-        a, b, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, kOneE8M0, 0, kOneE8M0);
+        a, b, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
 }
 
 // Power-of-two scales applied by the instruction itself: lane l's scale

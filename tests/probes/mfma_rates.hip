@@ -6,14 +6,14 @@
 // one workgroup per compute unit.  Each wave owns a 64x128 FP32 accumulator
 // tile and repeatedly runs one K step of it on register-resident FP8
 // fragments, as the GEMM's compute slots do, with no LDS or memory traffic:
-//   16x16x128 : 32 v_mfma_scale_f32_16x16x128_f8f6f4 per step (unit E8M0
-//               scales), either accumulating in place or writing a fresh
+//   16x16x128 : 32 v_mfma_f32_16x16x128_f8f6f4 per step (the GEMM's
+//               unscaled instruction), either accumulating in place or writing a fresh
 //               partial sum that an FP32 FMA promotes four instructions
 //               later (the FP32-scale GEMM's promotion), or -- "row x
 //               column", the weight-gradient GEMM's per-row scales on both
 //               operands -- with four products of a row scale and four
 //               column scales ahead of the four FMAs;
-//   32x32x64  : 16 v_mfma_scale_f32_32x32x64_f8f6f4, chained in pairs over
+//   32x32x64  : 16 v_mfma_f32_32x32x64_f8f6f4, chained in pairs over
 //               one 128-wide K block, either in place or into a partial sum
 //               promoted with 16 FMAs two blocks later.
 // "2 waves/SIMD": all 8 waves compute; "1 wave/SIMD": waves 4-7 leave at
@@ -41,13 +41,13 @@ typedef float v16f __attribute__((ext_vector_type(16)));
         }                                                                                       \
     } while (0)
 
-constexpr int kOne = 127;   // E8M0 2^0
-
+// Zero scale operands: the compiler emits the plain (unscaled) instruction,
+// as the GEMM's FP32-scale path does.
 __device__ __forceinline__ v4f mf16(const v8i& a, const v8i& b, const v4f& c) {
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, kOne, 0, kOne);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 __device__ __forceinline__ v16f mf32(const v8i& a, const v8i& b, const v16f& c) {
-    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kOne, 0, kOne);
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
 enum { k16InPlace, k16Promote, k32InPlace, k32Promote, k16PromoteRow };
