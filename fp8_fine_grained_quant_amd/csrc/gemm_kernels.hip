@@ -123,10 +123,10 @@ __device__ __forceinline__ v8i frag32(const uint8_t* __restrict__ slab, int bloc
 
 // The partial sum of one 128-wide K block, unscaled.  Zero scale operands
 // make the compiler emit the plain v_mfma_f32_16x16x128_f8f6f4, which has
-// no scale operands; a probe found it bitwise equal to the scaled form with
-// unit (E8M0 127) scales on 262,144 random outputs, and it issues faster
-// (Fprop 781.6 -> 774.8 us, Dgrad 821.6 -> 813.7 us, Wgrad 118.8 -> 115.1
-// us, bitwise identical).
+// no scale operands; it is bitwise equal to the scaled form with unit (E8M0
+// 127) scales (tests/probes/mfma_forms.hip: 262,144 random outputs), and it
+// issues faster (Fprop 781.6 -> 774.8 us, Dgrad 821.6 -> 813.7 us, Wgrad
+// 118.8 -> 115.1 us, bitwise identical).
 __device__ __forceinline__ v4f mfma_f8(const v8i& a, const v8i& b) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
         a, b, (v4f){0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
