@@ -474,10 +474,11 @@ __device__ __forceinline__ void slot_barrier_vm9() {
 // the FMAs that promote it (the ring of partial sums holds distance + 1).
 // An FMA that reads a result still in flight holds up the wave's in-order
 // issue, and with it the matrix pipe; at distance 4 the result has landed.
-// The grouped kernel runs 2-4 % faster at distance 6 (and 7); the dense ones
-// are the same at 4, 5 and 6, and keep 4 for its 8 fewer VGPRs.
-constexpr int kPromoteDistDense = 4;
-constexpr int kPromoteDistGrouped = 6;
+// The dense kernels run the same at 4, 5 and 6 (ROW128: 121.7, 122.6, 123.0
+// us on Wgrad).  The grouped kernel ran 2-4 % faster at 6 while it issued
+// the scaled matrix instruction; with the plain one, 4 is ~1 % faster than 6
+// on the MoE routing (3451 against 3485 us, bitwise identical).
+constexpr int kPromoteDist = 4;
 
 // Column scales of the current compute half in ROW128 mode: for column block
 // jj, this lane's 4 FP32 column scales, or (POW2) the E8M0 exponent of the
@@ -520,7 +521,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_pp_kernel(GemmParams p) {
     // VALU instructions of one promotion: FMAs, plus (ROW128) the products of
     // the row scale with the four column scales
     constexpr int kPromoteValu = ROW ? 8 : 4;
-    constexpr int kPromoteDist = GROUPED ? kPromoteDistGrouped : kPromoteDistDense;
     constexpr int kPartRing = kPromoteDist + 1;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_ab[2][kStageBytes];
     // [stage][0..255]: sa of the tile's rows.  [stage][256 + c]: BLOCK128 --
