@@ -226,7 +226,7 @@ FP8Q_API int fp8_dispatch_rows(const uint8_t* q_src, int64_t ldq_src, const floa
     if (ldq_src < cols || ldq_dst < cols || lds_src < src_rows || lds_dst < rows)
         return FP8Q_EINVAL;
     if (!aligned(s_src, 4) || !aligned(s_dst, 4) || !aligned(index, 4)) return FP8Q_EALIGN;
-    if ((rows + 31) / 32 > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;  // grid size
+    if ((rows + 255) / 256 * 8 > 0x7FFFFFFF) return FP8Q_EUNSUPPORTED;  // grid size
     fp8q::DispatchParams p{};
     p.q_src = q_src; p.ldq_src = ldq_src; p.s_src = s_src; p.lds_src = lds_src;
     p.src_rows = src_rows; p.index = index; p.rows = rows; p.cols = cols;
