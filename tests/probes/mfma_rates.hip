@@ -115,9 +115,18 @@ __global__ __launch_bounds__(512, 1) void probe(const int* __restrict__ seed, fl
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                // as if the fragments were reloaded for every half step
+                // as if the fragments and scales were reloaded for every half
+                // step (loop-invariant scale products would otherwise leave
+                // the loop, and row x column would issue 4 VALU instructions
+                // per matrix instruction instead of the GEMM's 8)
                 asm volatile("" : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]),
                                   "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
+                asm volatile("" : "+v"(sc[0]), "+v"(sc[1]), "+v"(sc[2]), "+v"(sc[3]));
+                if constexpr (MODE == k16PromoteRow)
+                    asm volatile("" : "+v"(cs[0].x), "+v"(cs[0].y), "+v"(cs[0].z), "+v"(cs[0].w),
+                                      "+v"(cs[1].x), "+v"(cs[1].y), "+v"(cs[1].z), "+v"(cs[1].w),
+                                      "+v"(cs[2].x), "+v"(cs[2].y), "+v"(cs[2].z), "+v"(cs[2].w),
+                                      "+v"(cs[3].x), "+v"(cs[3].y), "+v"(cs[3].z), "+v"(cs[3].w));
             }
         }
 #pragma unroll
@@ -172,6 +181,7 @@ __global__ __launch_bounds__(512, 1) void probe(const int* __restrict__ seed, fl
                 __builtin_amdgcn_sched_barrier(0);
                 asm volatile("" : "+v"(af[0]), "+v"(af[1]), "+v"(af[2]), "+v"(af[3]), "+v"(bf[0]),
                                   "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
+                asm volatile("" : "+v"(sc[0]), "+v"(sc[1]));
             }
         }
 #pragma unroll

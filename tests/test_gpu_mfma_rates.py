@@ -1,5 +1,5 @@
 """Throughput of the GEMM's compute slot on the full chip, register-only
-(tests/probes/mfma_rates.hip): the 16x16x128 and 32x32x64 scaled FP8 matrix
+(tests/probes/mfma_rates.hip): the 16x16x128 and 32x32x64 FP8 matrix
 instructions, accumulating in place or with the FP32 promotion of a fresh
 partial sum per 128-wide K block (jp-study.kr page, Figure 7(b)), with two or
 one computing waves per SIMD.  The table it prints backs the choice of
