@@ -50,10 +50,12 @@ def _enc(oracle, v):
     return c
 
 
-def _exact_case(oracle, M, N, K, seed, row_scales=False):
+def _exact_case(oracle, M, N, K, seed, row_scales=False, e_range=(-30, 30), v_range=(-10, 10),
+                with_delta=True):
     """Codes, scales and the exact C* (float64) of one constructed case.
     row_scales: B scales per column per K block (ROW128) instead of per
-    128x128 block."""
+    128x128 block.  e_range / v_range: exponents of the block-0 A and B
+    scales (half-open); with_delta=False leaves block 1 empty."""
     rng = np.random.default_rng(seed)
     nkb = K // 128
     assert nkb >= 2
@@ -65,7 +67,7 @@ def _exact_case(oracle, M, N, K, seed, row_scales=False):
             qa[np.arange(M), kb * 128 + seg * SEG + j] = one
     H = rng.integers(256, 512, (NSEG, N))
     sgn = rng.choice([-1.0, 1.0], (NSEG, N))
-    delta = rng.choice([-1.0, 0.0, 0.0, 1.0], (NSEG, N))
+    delta = rng.choice([-1.0, 0.0, 0.0, 1.0], (NSEG, N)) if with_delta else np.zeros((NSEG, N))
     qb = np.zeros((N, K), np.uint8)
     for s in range(NSEG):
         qb[:, s * SEG] = _enc(oracle, sgn[s] * 256.0)
@@ -73,19 +75,19 @@ def _exact_case(oracle, M, N, K, seed, row_scales=False):
             bit = ((H[s] - 256) >> b) & 1
             qb[:, s * SEG + 1 + (7 - b)] = np.where(bit == 1, _enc(oracle, sgn[s] * 2.0 ** b), 0)
         qb[:, 128 + s * SEG] = np.where(delta[s] != 0, _enc(oracle, delta[s]), 0)
-    e = rng.integers(-30, 30, M)
+    e = rng.integers(e_range[0], e_range[1], M)
     sa = np.empty((nkb, M), np.float32)
     sa[0] = np.ldexp(1.0, e)
     sa[1] = np.ldexp(1.0, e - 15)
     sa[2:] = np.ldexp(1.0, rng.integers(-20, 20, (nkb - 2, M)))
     nbn = (N + 127) // 128
     if row_scales:
-        v_col = rng.integers(-10, 10, N)
+        v_col = rng.integers(v_range[0], v_range[1], N)
         sb = np.empty((nkb, N), np.float32)
         sb[0] = sb[1] = np.ldexp(1.0, v_col)
         sb[2:] = np.ldexp(1.0, rng.integers(-20, 20, (nkb - 2, N)))
     else:
-        v_blk = rng.integers(-10, 10, nbn)
+        v_blk = rng.integers(v_range[0], v_range[1], nbn)
         sb = np.empty((nbn, nkb), np.float32)
         sb[:, 0] = sb[:, 1] = np.ldexp(1.0, v_blk)
         sb[:, 2:] = np.ldexp(1.0, rng.integers(-20, 20, (nbn, nkb - 2)))
@@ -100,8 +102,9 @@ def _exact_case(oracle, M, N, K, seed, row_scales=False):
 
 
 def _bf16_rne_bits(c: np.ndarray) -> np.ndarray:
-    """BF16 bit pattern nearest to each (FP32-representable, finite, normal
-    range) value, ties to the even significand -- from the definition."""
+    """BF16 bit pattern nearest to each FP32-representable finite value
+    (subnormals included: the neighbours are the bit patterns either side),
+    ties to the even significand -- from the definition."""
     f = c.astype(np.float32)
     u = f.view(np.uint32)
     lo_bits = (u >> 16).astype(np.uint32)                      # toward zero
@@ -125,6 +128,15 @@ def test_bf16_rne_definition_cases():
     assert np.array_equal(got, want)
     t = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
     assert np.array_equal(t.view(np.uint16), _bf16_rne_bits(vals))
+    # BF16 subnormals: ulp 2^-133; halfway cases go to the even pattern,
+    # half the smallest one to zero
+    u = 2.0 ** -133
+    sub = np.array([3 * u, 2.5 * u, 3.5 * u, 0.5 * u, 0.75 * u, 1.5 * u, -2.5 * u], np.float64)
+    want = np.array([3 * u, 2 * u, 4 * u, 0.0, u, 2 * u, -2 * u], np.float64)
+    got = (_bf16_rne_bits(sub).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, want)
+    t = torch.from_numpy(sub.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(t.view(np.uint16), _bf16_rne_bits(sub))
 
 
 @pytest.mark.gpu
@@ -164,6 +176,54 @@ def test_epilogue_bits_exact(fq, oracle, M, N, K, row):
                            f"{got16[tuple(bad[0])]:#06x} want {want_bf16[tuple(bad[0])]:#06x}")
     print(f"{M}x{N}x{K} row={row}: {n_down} ties down, {n_up} ties up, {n_off} one ulp off; "
           "FP32 and BF16 outputs bit-exact")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("row", [False, True])
+def test_epilogue_bits_exact_subnormal(fq, oracle, row):
+    """Outputs in the FP32 and BF16 subnormal range: block-0 scale exponents
+    e + v in [-149, -130], so C* = +-H * 2^(e+v) runs from normal values down
+    to a few FP32 ulps of 2^-149, every one exact in FP32 (the kernel's scale
+    product and FMA are exact there unless denormals were flushed).  BF16
+    rounds at its subnormal ulp 2^-133, with ties and underflow to zero."""
+    M, N, K = 256, 256, 256
+    qa, sa, qb, sb, c_star, _, _ = _exact_case(oracle, M, N, K, 4242 + row, row,
+                                               e_range=(-74, -64), v_range=(-75, -65),
+                                               with_delta=False)
+    mode = oracle.SCALE_ROW128 if row else oracle.SCALE_BLOCK128
+    c_o, _ = oracle.gemm_exact(qa, sa, qb, sb, mode=mode)
+    assert np.array_equal(c_o, c_star), "oracle disagrees with the constructed C*"
+    want_bf16 = _bf16_rne_bits(c_star)
+    cpu = torch.from_numpy(c_star.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(cpu.view(np.uint16), want_bf16)
+    mag = np.abs(c_star)
+    sub32 = int(((mag > 0) & (mag < 2.0 ** -126)).sum())
+    zero16 = int((want_bf16 & 0x7FFF == 0).sum())
+    sub16 = int((((want_bf16 & 0x7F80) == 0) & ((want_bf16 & 0x7F) != 0)).sum())
+    # exactly half a BF16 subnormal ulp (2^-133) from both neighbours
+    ties = int(((mag < 2.0 ** -126) & (np.ldexp(mag, 134) % 2 == 1)).sum())
+    assert sub32 > 1000 and zero16 > 50 and sub16 > 1000 and ties > 50, (sub32, zero16, sub16, ties)
+
+    a = torch.from_numpy(qa).cuda()
+    b = torch.from_numpy(qb).cuda()
+    sa_d = torch.from_numpy(sa).cuda()
+    sb_d = torch.from_numpy(sb).cuda()
+    smode = fq.SCALE_ROW128 if row else fq.SCALE_BLOCK128
+    c32 = fq.fp8_blockscaled_gemm(a, sa_d, b, sb_d, out_dtype=torch.float32, scale_mode=smode)
+    c16 = fq.fp8_blockscaled_gemm(a, sa_d, b, sb_d, out_dtype=torch.bfloat16, scale_mode=smode)
+    torch.cuda.synchronize()
+    got32 = np.ascontiguousarray(c32.cpu().numpy()).view(np.uint32)
+    want32 = c_star.astype(np.float32).view(np.uint32)
+    bad = np.argwhere(got32 != want32)
+    assert bad.size == 0, (f"FP32 output not exact at {len(bad)} elements, first {tuple(bad[0])}: "
+                           f"{got32[tuple(bad[0])]:#x} want {want32[tuple(bad[0])]:#x}")
+    got16 = np.ascontiguousarray(c16.view(torch.int16).cpu().numpy()).view(np.uint16)
+    bad = np.argwhere(got16 != want_bf16)
+    assert bad.size == 0, (f"BF16 output not RNE(C*) at {len(bad)} elements, first "
+                           f"{tuple(bad[0])}: C* {c_star[tuple(bad[0])]!r} got "
+                           f"{got16[tuple(bad[0])]:#06x} want {want_bf16[tuple(bad[0])]:#06x}")
+    print(f"row={row}: {sub32} FP32 subnormal outputs, {sub16} BF16 subnormal, {zero16} BF16 zeros, "
+          f"{ties} BF16 ties; bit-exact")
 
 
 @pytest.mark.gpu
