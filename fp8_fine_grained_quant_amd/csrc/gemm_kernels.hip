@@ -367,8 +367,7 @@ __device__ __forceinline__ void store_tile(const GemmParams& p, const v4f (&acc)
             } else {
                 const int ch = 2 * jj + (kq >> 1);
                 *reinterpret_cast<uint2*>(buf + r16 * 256 + ((ch ^ r16) << 4) + (kq & 1) * 8) =
-                    make_uint2(float_to_bf16_bits(v[0]) | (float_to_bf16_bits(v[1]) << 16),
-                               float_to_bf16_bits(v[2]) | (float_to_bf16_bits(v[3]) << 16));
+                    make_uint2(bf16x2_bits(v[0], v[1]), bf16x2_bits(v[2], v[3]));
             }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
