@@ -104,14 +104,17 @@ __device__ __forceinline__ void load8_elems(const void* row, int64_t c0, int64_t
 
 // Stores the 8 code bytes of [c0, c0+8) (those below `cols`); `vec`: the
 // row start is 8-byte aligned, so full runs use one 8-byte store.  Plain
-// (temporal) stores: the codes are read next by the GEMM, and kept in the
-// memory-side cache they need not come back from HBM (measured: the Fprop
-// GEMM after the quantizers runs ~1-2 % faster than after non-temporal
-// stores).
+// (temporal) stores by default: the codes are read next by the GEMM, and
+// kept in the memory-side cache they need not come back from HBM (measured:
+// the Fprop GEMM after the quantizers runs ~1-2 % faster than after
+// non-temporal stores).  `nt`: non-temporal, for outputs too large for that
+// cache.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ void store8(uint8_t* row, int64_t c0, int64_t cols, uint32_t lo,
-                                       uint32_t hi, bool vec) {
+                                       uint32_t hi, bool vec, bool nt = false) {
     if (vec && c0 + 8 <= cols) {
-        *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
+        if (nt) __builtin_nontemporal_store((u32x2){lo, hi}, reinterpret_cast<u32x2*>(row + c0));
+        else *reinterpret_cast<uint2*>(row + c0) = make_uint2(lo, hi);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
                                                          uint8_t* __restrict__ q, int64_t ldq,
                                                          uint8_t* __restrict__ qt, int64_t ldqt,
                                                          float* __restrict__ s, int64_t lds,
-                                                         int64_t tiles_c, bool vin, bool vq,
+                                                         int64_t tiles_c, bool vin, int vq,
                                                          int vqt) {
     static_assert(MODE == kTileBlock || MODE == kTileRows, "128x1 groups: quant_cols_kernel");
     static_assert(TH == 128 || MODE == kTileRows, "only 1x128 groups allow short tiles");
@@ -358,7 +361,7 @@ __global__ __launch_bounds__(2 * TH) void quant_tile_kernel(const void* __restri
     if (q != nullptr) {
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
-            if (r0 + p < rows) store8(q + (r0 + p) * ldq, c0, cols, lo[p], hi[p], vq);
+            if (r0 + p < rows) store8(q + (r0 + p) * ldq, c0, cols, lo[p], hi[p], vq != 0, vq == 2);
         }
     }
     if (MODE == kTileBlock && qt != nullptr) {
@@ -549,12 +552,22 @@ hipError_t launch_quant_rows(const void* x, int dtype, int64_t rows, int64_t col
     return launch_rows_t<kF32, kRuleFP32>(x, rows, cols, ldx, q, ldq, s, lds, vin, vout, stream);
 }
 
+// Code output size above which the tile kernel stores codes non-temporally.
+constexpr int64_t kNtCodeBytes = int64_t(256) << 20;
+
 hipError_t launch_quant_tiles(const void* x, int dtype, int mode, int64_t rows, int64_t cols,
                               int64_t ldx, uint8_t* q, int64_t ldq, uint8_t* qt, int64_t ldqt,
                               float* s, int64_t lds, int rule, hipStream_t stream) {
     const int64_t esz = dtype == kBF16 ? 2 : 4;
     const bool vin = is_aligned(x, 16) && (ldx * esz) % 16 == 0;
-    const bool vq = q != nullptr && is_aligned(q, 8) && ldq % 8 == 0;
+    // row-major codes: 0 byte stores, 1 8-byte stores, 2 8-byte non-temporal
+    // stores (outputs larger than the 256 MB memory-side cache cannot stay
+    // there for the next kernel, and ordinary stores would only evict what
+    // can: MoE W_e codes, 3.76 GB, 1940 -> 1880 us; the 235 MB of MoE token
+    // codes stay ordinary, 107 against 120 us non-temporal)
+    const int vq = q == nullptr || !is_aligned(q, 8) || ldq % 8 != 0 ? 0
+                   : rows * cols > kNtCodeBytes                     ? 2
+                                                                    : 1;
     const int vqt = qt == nullptr ? 0
                     : (is_aligned(qt, 16) && ldqt % 16 == 0) ? 2
                     : (is_aligned(qt, 8) && ldqt % 8 == 0) ? 1
